@@ -1,0 +1,86 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversions, MFMA operand
+// types and the int4 -> bf16 operand conversion used on the weight load path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float fp16_to_f32(uint16_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
+// Fragment k-order.  An MFMA lane holds 8 consecutive-k operands of one row
+// (A) or one column (B).  A byte of int4 codes holds k = 2m and 2m+1, so the
+// cheap mask-and-or conversion below produces the 8 codes of a 32-bit word in
+// the order k = 0,4,1,5,2,6,3,7.  The contraction over k does not care about
+// the order as long as A uses the same one, so every A fragment is put in that
+// order too (permute_a for natural-order rows; the gate/up kernel stores h
+// already in this order, see h_phys_col).
+
+// Four 32-bit words of 8 natural-order bf16 -> the 0,4,1,5,2,6,3,7 order.
+__device__ __forceinline__ u32x4 permute_a(u32x4 a) {
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(a.z, a.x, 0x05040100u);  // (k0, k4)
+  r.y = __builtin_amdgcn_perm(a.z, a.x, 0x07060302u);  // (k1, k5)
+  r.z = __builtin_amdgcn_perm(a.w, a.y, 0x05040100u);  // (k2, k6)
+  r.w = __builtin_amdgcn_perm(a.w, a.y, 0x07060302u);  // (k3, k7)
+  return r;
+}
+
+// Physical position, inside its group of 8, of logical column i of h.
+__device__ __forceinline__ int h_phys_col(int n) {
+  return (n & ~7) | ((n & 3) << 1) | ((n >> 2) & 1);
+}
+
+// int4 dequantisation on the load path.  OR-ing a code q (0..15) into the
+// mantissa of bf16 128.0 (0x4300) gives exactly 128 + q, so one 32-bit word
+// of 8 codes becomes four bf16 pairs with a shift and an and-or each.  The
+// MFMA then accumulates sum_k a_k (128 + q_k); the per-row scale s and
+// zero-point z are applied once per output in the epilogue:
+//     sum_k a_k (q_k - z) s = s * (acc - (128 + z) * sum_k a_k).
+constexpr float kCodeBias = 128.0f;
+
+__device__ __forceinline__ u32x4 codes_to_bf16(uint32_t w) {
+  u32x4 r;
+  r.x = (w & 0x000F000Fu) | 0x43004300u;          // (q0, q4)
+  r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;   // (q1, q5)
+  r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;   // (q2, q6)
+  r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;  // (q3, q7)
+  return r;
+}
+
+// bf16 1.0 in every slot: a B operand whose product gives row sums of A.
+__device__ __forceinline__ u32x4 ones_bf16() {
+  u32x4 r;
+  r.x = r.y = r.z = r.w = 0x3F803F80u;
+  return r;
+}
+
+// D += A(16x32) * B(32x16), bf16 in, fp32 accumulate.  Lane l holds A row
+// l%16 and B column l%16 for the k-slice of lane group l/16; D row
+// 4*(l/16) + i, column l%16 sits in element i.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+}  // namespace moe

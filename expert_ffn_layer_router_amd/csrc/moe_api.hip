@@ -1,0 +1,298 @@
+// C ABI of the MoE FFN layer forward: argument checks, the workspace plan,
+// the launch sequence, HIP-graph capture and replay, status reporting.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "moe.h"
+#include "plan.h"
+
+#define MOE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr uint32_t kMagic = 0x4d6f4531u;  // "MoE1"
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int largest_divisor_at_most(int n, int cap) {
+  cap = std::max(1, std::min(cap, n));
+  for (int q = cap; q >= 1; --q)
+    if (n % q == 0) return q;
+  return 1;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+struct moe_layer {
+  uint32_t magic = kMagic;
+  moe_config cfg{};
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace moe {
+
+void make_plan(const moe_config& c, int T, Plan* p) {
+  *p = Plan{};
+  p->T = T;
+  p->R = T * c.top_k;
+  const int E = c.num_experts;
+  // router: enough blocks to cover the chip when T is small
+  const int chunks = c.d_model / kRouterKChunk;
+  const int router_blocks = ((T + kRouterTokTile - 1) / kRouterTokTile) * ((E + kRouterExpTile - 1) / kRouterExpTile);
+  p->router_split = largest_divisor_at_most(chunks, std::max(1, 512 / std::max(1, router_blocks)));
+  // GEMM row tiles: sum_e ceil(c_e / rows) <= ceil(R / rows) + (non-empty experts)
+  p->max_tiles = (p->R + kTileRows - 1) / kTileRows + std::min(E, p->R);
+  // split the down projection's k range until ~4 blocks per compute unit
+  const int down_blocks = std::max(1, p->max_tiles * (c.d_model / kGemmColsPerBlock));
+  p->down_split = largest_divisor_at_most(c.d_ff / kGemmKStep, (1024 + down_blocks - 1) / down_blocks);
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  const size_t R = (size_t)p->R;
+  p->flags = take(4);
+  p->logit_part = take(sizeof(double) * (size_t)p->router_split * T * E);
+  p->topk_idx = take(4 * R);
+  p->topk_w = take(4 * R);
+  p->counts = take(4 * (size_t)E);
+  p->offsets = take(4 * (size_t)(E + 1));
+  p->perm = take(4 * R);
+  p->inv = take(4 * R);
+  p->tile_e = take(4 * (size_t)p->max_tiles);
+  p->tile_r0 = take(4 * (size_t)p->max_tiles);
+  p->num_tiles = take(4);
+  p->h = take(2 * R * (size_t)c.d_ff);
+  p->y = take(4 * (size_t)p->down_split * R * (size_t)c.d_model);
+  p->total = off;
+}
+
+}  // namespace moe
+
+namespace {
+
+moe_status check_handle(moe_handle h) {
+  if (!h || h->magic != kMagic) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
+  return MOE_OK;
+}
+
+moe_status check_T(const moe_layer* h, int32_t T) {
+  if (T < 0 || T > h->cfg.max_tokens)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T=%d outside [0, max_tokens=%d]", T, h->cfg.max_tokens);
+  return MOE_OK;
+}
+
+moe_status check_forward_args(moe_handle h, int32_t T, const uint16_t* hidden, const float* router_w,
+                              const float* router_bias, const int32_t* slot_table, const moe_weights* w,
+                              uint16_t* out, void* workspace, size_t workspace_bytes, moe::Plan* plan) {
+  moe_status st = check_handle(h);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(h, T)) != MOE_OK) return st;
+  moe::make_plan(h->cfg, T, plan);
+  if (T == 0) return MOE_OK;
+  if (!hidden || !router_w || !slot_table || !w || !out || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  if (!w->w_gate || !w->w_up || !w->w_down || !w->s_gate || !w->z_gate || !w->s_up || !w->z_up ||
+      !w->s_down || !w->z_down)
+    return fail(MOE_ERR_INVALID_ARG, "null pointer in moe_weights");
+  const void* a16[] = {hidden, router_w, out, workspace, w->w_gate, w->w_up, w->w_down};
+  for (const void* p : a16)
+    if (!aligned(p, 16)) return fail(MOE_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+  const void* a4[] = {slot_table, router_bias};
+  for (const void* p : a4)
+    if (p && !aligned(p, 4)) return fail(MOE_ERR_INVALID_ARG, "pointer %p is not 4-byte aligned", p);
+  const void* a2[] = {w->s_gate, w->z_gate, w->s_up, w->z_up, w->s_down, w->z_down};
+  for (const void* p : a2)
+    if (!aligned(p, 2)) return fail(MOE_ERR_INVALID_ARG, "pointer %p is not 2-byte aligned", p);
+  if (workspace_bytes < plan->total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, T=%d needs %zu", workspace_bytes, T,
+                plan->total);
+  return MOE_OK;
+}
+
+moe_status enqueue(const moe_layer* h, const moe::Plan& p, const uint16_t* hidden, const float* router_w,
+                   const float* router_bias, const int32_t* slot_table, const moe_weights* w, uint16_t* out,
+                   void* workspace, hipStream_t s) {
+  char* ws = static_cast<char*>(workspace);
+  moe::launch_router(h->cfg, p, hidden, router_w, router_bias, ws, s);
+  moe::launch_permute(h->cfg, p, ws, s);
+  moe::launch_gemms(h->cfg, p, hidden, slot_table, *w, ws, s);
+  moe::launch_combine(h->cfg, p, out, ws, s);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return MOE_OK;
+}
+
+void drop_graph(moe_layer* h) {
+  if (h->exec) (void)hipGraphExecDestroy(h->exec);
+  if (h->graph) (void)hipGraphDestroy(h->graph);
+  h->exec = nullptr;
+  h->graph = nullptr;
+}
+
+}  // namespace
+
+MOE_EXPORT moe_status moe_create(const moe_config* cfg, moe_handle* out) {
+  if (!cfg || !out) return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  *out = nullptr;
+  const moe_config& c = *cfg;
+  if (c.flags != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "flags must be 0");
+  if (c.d_model <= 0 || c.d_model % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "d_model=%d must be a positive multiple of 128", c.d_model);
+  if (c.d_ff <= 0 || c.d_ff % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "d_ff=%d must be a positive multiple of 128", c.d_ff);
+  if (c.num_experts < 1 || c.num_experts > 256)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "num_experts=%d outside [1, 256]", c.num_experts);
+  if (c.top_k < 1 || c.top_k > std::min(c.num_experts, 8))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "top_k=%d outside [1, min(E, 8)]", c.top_k);
+  if (c.num_slots < 1) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "num_slots=%d must be >= 1", c.num_slots);
+  if (c.max_tokens < 1 || c.max_tokens > 65536)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tokens=%d outside [1, 65536]", c.max_tokens);
+  moe_layer* h = new (std::nothrow) moe_layer;
+  if (!h) return fail(MOE_ERR_INVALID_ARG, "out of host memory");
+  h->cfg = c;
+  *out = h;
+  return MOE_OK;
+}
+
+MOE_EXPORT void moe_destroy(moe_handle h) {
+  if (!h || h->magic != kMagic) return;
+  drop_graph(h);
+  h->magic = 0;
+  delete h;
+}
+
+MOE_EXPORT moe_status moe_workspace_size(moe_handle h, int32_t T, size_t* bytes) {
+  moe_status st = check_handle(h);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  if ((st = check_T(h, T)) != MOE_OK) return st;
+  moe::Plan p;
+  moe::make_plan(h->cfg, T, &p);
+  *bytes = p.total;
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_forward(moe_handle h, int32_t T, const uint16_t* hidden, const float* router_w,
+                                  const float* router_bias, const int32_t* slot_table, const moe_weights* w,
+                                  uint16_t* out, void* workspace, size_t workspace_bytes, moe_stream stream) {
+  moe::Plan p;
+  moe_status st = check_forward_args(h, T, hidden, router_w, router_bias, slot_table, w, out, workspace,
+                                     workspace_bytes, &p);
+  if (st != MOE_OK || T == 0) return st;
+  return enqueue(h, p, hidden, router_w, router_bias, slot_table, w, out, workspace,
+                 static_cast<hipStream_t>(stream));
+}
+
+MOE_EXPORT moe_status moe_routing_view(moe_handle h, const void* workspace, int32_t T, moe_routing* view) {
+  moe_status st = check_handle(h);
+  if (st != MOE_OK) return st;
+  if (!workspace || !view) return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  if ((st = check_T(h, T)) != MOE_OK) return st;
+  moe::Plan p;
+  moe::make_plan(h->cfg, T, &p);
+  const char* ws = static_cast<const char*>(workspace);
+  view->topk_idx = reinterpret_cast<const int32_t*>(ws + p.topk_idx);
+  view->topk_w = reinterpret_cast<const float*>(ws + p.topk_w);
+  view->counts = reinterpret_cast<const int32_t*>(ws + p.counts);
+  view->offsets = reinterpret_cast<const int32_t*>(ws + p.offsets);
+  view->perm = reinterpret_cast<const int32_t*>(ws + p.perm);
+  view->inv_perm = reinterpret_cast<const int32_t*>(ws + p.inv);
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_graph_capture(moe_handle h, int32_t T, const uint16_t* hidden, const float* router_w,
+                                        const float* router_bias, const int32_t* slot_table,
+                                        const moe_weights* w, uint16_t* out, void* workspace,
+                                        size_t workspace_bytes, moe_stream stream) {
+  moe::Plan p;
+  moe_status st = check_forward_args(h, T, hidden, router_w, router_bias, slot_table, w, out, workspace,
+                                     workspace_bytes, &p);
+  if (st != MOE_OK) return st;
+  if (!stream) return fail(MOE_ERR_INVALID_ARG, "graph capture needs a non-null stream");
+  if (T == 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "graph capture needs T > 0");
+  drop_graph(h);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(err));
+  const moe_status est = enqueue(h, p, hidden, router_w, router_bias, slot_table, w, out, workspace, s);
+  hipGraph_t graph = nullptr;
+  err = hipStreamEndCapture(s, &graph);
+  if (est != MOE_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return est;
+  }
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(err));
+  hipGraphExec_t exec = nullptr;
+  err = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (err != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return fail(MOE_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(err));
+  }
+  h->graph = graph;
+  h->exec = exec;
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_graph_launch(moe_handle h, moe_stream stream) {
+  moe_status st = check_handle(h);
+  if (st != MOE_OK) return st;
+  if (!h->exec) return fail(MOE_ERR_BAD_STATE, "no captured graph");
+  const hipError_t err = hipGraphLaunch(h->exec, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGraphLaunch: %s", hipGetErrorString(err));
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_device_flags(moe_handle h, const void* workspace, int32_t T, moe_stream stream,
+                                       uint32_t* flags) {
+  moe_status st = check_handle(h);
+  if (st != MOE_OK) return st;
+  if (!workspace || !flags) return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  if ((st = check_T(h, T)) != MOE_OK) return st;
+  moe::Plan p;
+  moe::make_plan(h->cfg, T, &p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t err = hipMemcpyAsync(&v, static_cast<const char*>(workspace) + p.flags, sizeof v,
+                                  hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "reading device flags: %s", hipGetErrorString(err));
+  *flags = v;
+  return MOE_OK;
+}
+
+MOE_EXPORT const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_BAD_STATE: return "MOE_ERR_BAD_STATE";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+MOE_EXPORT const char* moe_last_error(void) { return g_last_error.c_str(); }

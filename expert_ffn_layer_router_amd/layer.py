@@ -1,0 +1,140 @@
+"""Python face of the C ABI.  torch supplies device memory and the stream;
+every step of the layer runs in the library's HIP kernels."""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+
+WEIGHT_FIELDS = ("w_gate", "w_up", "w_down", "s_gate", "z_gate", "s_up", "z_up", "s_down", "z_down")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def to_device(arr: np.ndarray, device="cuda"):
+    """numpy -> torch on `device`; uint16 arrays keep their bit patterns (int16)."""
+    torch = _torch()
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+@dataclasses.dataclass
+class DeviceWeights:
+    """The slot-indexed int4 weight pool on the device (keeps the tensors alive)."""
+    tensors: dict
+
+    @classmethod
+    def upload(cls, weights, device="cuda") -> "DeviceWeights":
+        src = weights if isinstance(weights, dict) else {f: getattr(weights, f) for f in WEIGHT_FIELDS}
+        return cls({f: to_device(src[f], device) for f in WEIGHT_FIELDS})
+
+    def struct(self) -> _lib.MoeWeights:
+        return _lib.MoeWeights(**{f: _ptr(self.tensors[f]) for f in WEIGHT_FIELDS})
+
+
+class MoeLayer:
+    """One layer shape.  Mirrors moe_create / moe_forward / moe_routing_view /
+    moe_graph_capture / moe_graph_launch / moe_device_flags."""
+
+    def __init__(self, d_model: int, d_ff: int, num_experts: int, top_k: int, num_slots: int,
+                 max_tokens: int):
+        self.lib = _lib.load()
+        self.cfg = _lib.MoeConfig(d_model, d_ff, num_experts, top_k, num_slots, max_tokens, 0)
+        h = ctypes.c_void_p()
+        _lib.check(self.lib.moe_create(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self.handle = h
+        self._graph_keepalive = None
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.moe_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self, T: int) -> int:
+        n = ctypes.c_size_t()
+        _lib.check(self.lib.moe_workspace_size(self.handle, int(T), ctypes.byref(n)))
+        return n.value
+
+    def new_workspace(self, T: int, device="cuda"):
+        torch = _torch()
+        return torch.empty(max(self.workspace_size(T), 256), dtype=torch.uint8, device=device)
+
+    @staticmethod
+    def _stream(stream):
+        torch = _torch()
+        s = torch.cuda.current_stream() if stream is None else stream
+        return ctypes.c_void_p(int(s.cuda_stream))
+
+    def _args(self, hidden, router_w, router_b, slot_table, weights, out, workspace):
+        T = int(hidden.shape[0])
+        return (self.handle, T, _ptr(hidden), _ptr(router_w), _ptr(router_b), _ptr(slot_table),
+                ctypes.byref(weights.struct()), _ptr(out), _ptr(workspace),
+                int(workspace.numel() * workspace.element_size()))
+
+    def forward(self, hidden, router_w, router_b, slot_table, weights: DeviceWeights, out=None,
+                workspace=None, stream=None):
+        """hidden: bf16 (or int16 bit patterns) [T, d] on the device.  Returns out [T, d]."""
+        torch = _torch()
+        T = int(hidden.shape[0])
+        if out is None:
+            out = torch.empty((T, self.cfg.d_model), dtype=hidden.dtype, device=hidden.device)
+        if workspace is None:
+            workspace = self.new_workspace(T, hidden.device)
+        _lib.check(self.lib.moe_forward(*self._args(hidden, router_w, router_b, slot_table, weights, out,
+                                                    workspace), self._stream(stream)))
+        return out
+
+    def capture(self, hidden, router_w, router_b, slot_table, weights: DeviceWeights, out, workspace,
+                stream):
+        """Captures a forward into the handle's graph (buffers must outlive the graph)."""
+        _lib.check(self.lib.moe_graph_capture(*self._args(hidden, router_w, router_b, slot_table, weights,
+                                                          out, workspace), self._stream(stream)))
+        self._graph_keepalive = (hidden, router_w, router_b, slot_table, weights, out, workspace)
+
+    def replay(self, stream=None):
+        _lib.check(self.lib.moe_graph_launch(self.handle, self._stream(stream)))
+
+    def routing(self, workspace, T: int) -> dict:
+        """Views (into `workspace`) of the routing the last forward left there."""
+        torch = _torch()
+        v = _lib.MoeRouting()
+        _lib.check(self.lib.moe_routing_view(self.handle, _ptr(workspace), int(T), ctypes.byref(v)))
+        base = int(workspace.data_ptr())
+        k, E, R = self.cfg.top_k, self.cfg.num_experts, int(T) * self.cfg.top_k
+
+        def view(ptr, n, dtype):
+            off = int(ptr) - base
+            return workspace[off:off + 4 * n].view(dtype)
+
+        return dict(topk_idx=view(v.topk_idx, R, torch.int32).view(int(T), k),
+                    topk_w=view(v.topk_w, R, torch.float32).view(int(T), k),
+                    counts=view(v.counts, E, torch.int32),
+                    offsets=view(v.offsets, E + 1, torch.int32),
+                    perm=view(v.perm, R, torch.int32),
+                    inv_perm=view(v.inv_perm, R, torch.int32))
+
+    def device_flags(self, workspace, T: int, stream=None) -> int:
+        f = ctypes.c_uint32()
+        _lib.check(self.lib.moe_device_flags(self.handle, _ptr(workspace), int(T), self._stream(stream),
+                                             ctypes.byref(f)))
+        return int(f.value)

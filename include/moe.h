@@ -1,0 +1,155 @@
+/*
+ * moe.h -- C ABI of an MI355X (gfx950) Mixture-of-Experts FFN layer forward.
+ *
+ * One call evaluates, for T tokens,
+ *     out[t] = sum over token t's k chosen experts e of w[t,e] * FFN_e(x[t]),
+ *     FFN_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x)),
+ * with the expert weights stored as per-row int4 codes plus an fp16 scale and
+ * zero-point (W = (q - z) * s) and read through an expert-to-slot table.
+ *
+ * Where each step comes from (three web pages on expert offloading for MoE
+ * inference; the "Strata" page is titled "125B MoE at 100+ tok/s on an
+ * RTX 3090: a full-pipeline inference tuning record"):
+ *   routing       Strata page, section 1.1 (top-2 or top-1 experts per token);
+ *                 Co-inference page, section 5.1 (router kept at full precision)
+ *   regrouping    Strata page, section 4.2 (tokens reordered by expert id)
+ *   int4 experts  Strata page, section 3.1 (per-expert scale and zero-point,
+ *                 dequantised on the load path, not in a kernel of its own)
+ *   group GEMM    Strata page, section 3.2 (one batched product over the
+ *                 experts' contiguous token groups)
+ *   slots         Co-inference page, section 2.2 (experts held in GPU cache
+ *                 slots); Strata page, section 2.1 (hot-expert pool)
+ *   graph replay  Strata page, section 3.4 (the decode step captured once and
+ *                 replayed, with a fixed batch and buffers allocated first)
+ *
+ * Conventions shared by every entry point
+ *   - Every function returns a moe_status; no C++ exception crosses the ABI.
+ *     On failure moe_last_error() holds a message for the calling thread.
+ *   - Argument checks happen before anything is enqueued: a call that fails
+ *     validation has not touched the stream or device memory.
+ *   - Device pointers are caller-owned, must be 16-byte aligned, and must stay
+ *     valid until the enqueued work completes.  The library allocates no
+ *     device memory; all intermediates live in the caller's workspace.
+ *   - moe_forward and moe_graph_launch only enqueue work on `stream` (a
+ *     hipStream_t; NULL means the null stream): no host synchronisation.
+ *   - Calls that share one workspace must not overlap in time.
+ *   - bf16 and fp16 values are passed as their 16-bit patterns (uint16_t).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,          /* null pointer, bad handle, misaligned pointer */
+  MOE_ERR_UNSUPPORTED_SHAPE = 2,    /* a shape outside the supported set (see moe_create) */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < moe_workspace_size(T) */
+  MOE_ERR_HIP = 4,                  /* a HIP runtime call failed; detail in moe_last_error() */
+  MOE_ERR_BAD_STATE = 5             /* e.g. moe_graph_launch before a successful capture */
+} moe_status;
+
+/* Device error bits, reported by moe_device_flags. */
+#define MOE_FLAG_BAD_SLOT 0x1u      /* slot_table[e] outside [0, num_slots) for a routed expert;
+                                       that expert contributed zero */
+
+typedef struct moe_config {
+  int32_t d_model;      /* hidden width d; multiple of 128 */
+  int32_t d_ff;         /* expert inner width; multiple of 128 */
+  int32_t num_experts;  /* E, 1..256 */
+  int32_t top_k;        /* k, 1..min(E, 8) */
+  int32_t num_slots;    /* slots in the weight pool, >= 1 */
+  int32_t max_tokens;   /* largest T a call may pass, 1..65536 */
+  uint32_t flags;       /* reserved, must be 0 */
+} moe_config;
+
+/* Per-slot weight pool (device pointers, caller-owned).  Slot s of a matrix
+ * with N output rows and K inputs occupies N*K/2 bytes: row n holds K codes
+ * in 0..15, two per byte, the even k in the low nibble.  Scales and
+ * zero-points are fp16, one per output row, indexed by slot. */
+typedef struct moe_weights {
+  const uint8_t *w_gate;   /* [num_slots][d_ff][d_model/2] */
+  const uint8_t *w_up;     /* [num_slots][d_ff][d_model/2] */
+  const uint8_t *w_down;   /* [num_slots][d_model][d_ff/2] */
+  const uint16_t *s_gate, *z_gate;  /* [num_slots][d_ff] */
+  const uint16_t *s_up, *z_up;      /* [num_slots][d_ff] */
+  const uint16_t *s_down, *z_down;  /* [num_slots][d_model] */
+} moe_weights;
+
+/* Device pointers into a workspace after a forward with T tokens (R = T*k). */
+typedef struct moe_routing {
+  const int32_t *topk_idx;  /* [T][k]  chosen experts, logit descending, ties to lower id */
+  const float *topk_w;      /* [T][k]  softmax over the k chosen logits */
+  const int32_t *counts;    /* [E]     rows per expert */
+  const int32_t *offsets;   /* [E+1]   exclusive prefix sum of counts */
+  const int32_t *perm;      /* [R]     grouped position p -> assignment a = t*k + j */
+  const int32_t *inv_perm;  /* [R]     assignment a -> grouped position p */
+} moe_routing;
+
+typedef struct moe_layer *moe_handle;
+typedef void *moe_stream; /* a hipStream_t */
+
+/* Creates a handle for one layer shape.  Host only: no device call, no device
+ * allocation.  Returns MOE_ERR_UNSUPPORTED_SHAPE for shapes outside:
+ * d_model % 128 == 0, d_ff % 128 == 0, 1 <= E <= 256, 1 <= k <= min(E, 8),
+ * num_slots >= 1, 1 <= max_tokens <= 65536, flags == 0. */
+moe_status moe_create(const moe_config *cfg, moe_handle *out);
+
+/* Frees the handle and any captured graph.  NULL is ignored. */
+void moe_destroy(moe_handle h);
+
+/* Bytes of workspace a forward with T tokens needs (0 <= T <= max_tokens). */
+moe_status moe_workspace_size(moe_handle h, int32_t T, size_t *bytes);
+
+/* Enqueues the layer forward for T tokens (0 <= T <= max_tokens; T = 0 is a
+ * no-op returning MOE_OK).
+ *   hidden       bf16 [T][d_model]
+ *   router_w     fp32 [E][d_model]
+ *   router_bias  fp32 [E], or NULL for none
+ *   slot_table   int32 [E], device memory, read when the kernels run
+ *   w            the slot-indexed weight pool
+ *   out          bf16 [T][d_model]
+ *   workspace    at least moe_workspace_size(T) bytes; holds the routing
+ *                (see moe_routing_view) and the device error flags after the
+ *                call. */
+moe_status moe_forward(moe_handle h, int32_t T, const uint16_t *hidden, const float *router_w,
+                       const float *router_bias, const int32_t *slot_table, const moe_weights *w,
+                       uint16_t *out, void *workspace, size_t workspace_bytes, moe_stream stream);
+
+/* Fills `view` with device pointers to the routing a forward with T tokens
+ * left in `workspace`.  Pointer arithmetic only. */
+moe_status moe_routing_view(moe_handle h, const void *workspace, int32_t T, moe_routing *view);
+
+/* Captures the enqueue sequence of moe_forward (same arguments) into a HIP
+ * graph held by the handle, replacing any earlier capture.  The graph bakes
+ * in T and every pointer; the contents of hidden, router weights, the slot
+ * table and the weight pool are read at each replay, so the caller may
+ * rewrite them between launches.  `stream` must not be NULL. */
+moe_status moe_graph_capture(moe_handle h, int32_t T, const uint16_t *hidden, const float *router_w,
+                             const float *router_bias, const int32_t *slot_table, const moe_weights *w,
+                             uint16_t *out, void *workspace, size_t workspace_bytes, moe_stream stream);
+
+/* Replays the captured graph on `stream`.  MOE_ERR_BAD_STATE without a capture. */
+moe_status moe_graph_launch(moe_handle h, moe_stream stream);
+
+/* Waits for `stream`, then reads the MOE_FLAG_* bits the last forward on
+ * `workspace` raised.  Each forward clears the bits when it starts. */
+moe_status moe_device_flags(moe_handle h, const void *workspace, int32_t T, moe_stream stream,
+                            uint32_t *flags);
+
+/* Static text for a status code. */
+const char *moe_status_string(moe_status s);
+
+/* Detail of the calling thread's last failing call ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */
