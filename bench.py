@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE FFN layer forward on one MI355X.
+
+A step is one full layer forward (router top-k, regroup, int4 gate/up GEMM
+with SwiGLU, down GEMM, combine) over one batch of the workload.  Prints ONE
+JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--config mixtral_decode] [--mode graph|eager]
+
+Inputs are seeded synthetic layers (synth package) resident in HBM before
+timing starts.  Several copies of the weight pool are used in rotation so
+that a step never finds the previous step's weights in the 256 MB MALL (a
+model's successive layers have different weights).
+
+Extra modes for counter runs:
+    --copy-calibration   time a plain 1 GiB device copy (scale for FETCH/WRITE_SIZE)
+    --summarize-pmc DIR  fold a rocprofv3 --pmc output directory into a JSON summary
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; HBM GB/s (T=16 decode), MFMA util (T=2048 prefill)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20
+DECODE_BOUND = {"mixtral_decode": "hbm", "phi35_skew": "hbm", "fine_decode": "hbm", "tiny": "hbm",
+                "fine_tiny": "hbm", "mixtral_prefill": "mfma", "fine_prefill": "mfma"}
+KERNEL_OF_STAGE = {"gate_up": "gateup_swiglu_kernel", "down": "down_kernel"}
+GEMM_SOURCE = os.path.join(ROOT, "expert_ffn_layer_router_amd", "csrc", "grouped_gemm.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(path=GEMM_SOURCE) -> str:
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------- work accounting
+def algorithmic_work(shape, counts):
+    """Bytes and FLOPs the method itself must move / compute for one forward,
+    per kernel and for the layer (active experts only; no tile padding)."""
+    d, f, T, k, E = shape.d_model, shape.d_ff, shape.T, shape.top_k, shape.num_experts
+    R = T * k
+    active = int(sum(1 for c in counts if c > 0))
+    gate_up_w = active * (d * f + 2 * 2 * 2 * f)       # gate+up codes (2 x d*f/2) + fp16 s,z of both
+    down_w = active * (d * f // 2 + 2 * 2 * d)          # down codes + fp16 s,z
+    gate_up_bytes = gate_up_w + 2 * T * d + 2 * R * f   # + x rows read, h written (bf16)
+    down_bytes = down_w + 2 * R * f + 2 * R * d         # + h read, y written (bf16-equivalent)
+    layer_bytes = gate_up_w + down_w + 2 * T * d + 2 * T * d + 4 * E * d + 4 * E + 4 * E
+    return dict(active=active, R=R,
+                gate_up=dict(bytes=gate_up_bytes, flops=4 * R * d * f),
+                down=dict(bytes=down_bytes, flops=2 * R * d * f),
+                layer=dict(bytes=layer_bytes, flops=6 * R * d * f))
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(case, budget_s=15.0):
+    """The oracle (fp32 BLAS, routing in fp64) as it stands, timed on the host."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    shape, w = case.shape, case.weights
+    kw = {a: getattr(w, a) for a in w.ARRAYS}
+    n_tok = min(shape.T, 64)
+    tokens = None if n_tok == shape.T else np.arange(n_tok)
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        oracle.forward(case.hidden, top_k=shape.top_k, precision="f32", tokens=tokens, **kw)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end or len(times) >= 5:
+            break
+    med = statistics.median(times)
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+    except OSError:
+        pass
+    sample = (f"{n_tok} of {shape.T} tokens of the same workload, full forward incl. dequant of the "
+              f"experts they use, median of {len(times)} runs; host CPU: {cpu}")
+    return {"value": n_tok / med, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample,
+            "seconds_per_run": med}
+
+
+# --------------------------------------------------------------------------- PMC summaries
+def summarize_pmc(directory, out_path, calib_path=None):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from rocprofv3
+    --pmc CSV output under `directory`."""
+    import csv
+    per = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection*.csv"), recursive=True):
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                name = row.get("Kernel_Name", "")
+                ctr = row.get("Counter_Name", "")
+                try:
+                    val = float(row.get("Counter_Value", "nan"))
+                except ValueError:
+                    continue
+                disp = row.get("Dispatch_Id", "")
+                per.setdefault(name, {}).setdefault(ctr, {}).setdefault(disp, 0.0)
+                per[name][ctr][disp] += val
+    summary = {}
+    for name, ctrs in per.items():
+        summary[name] = {c: statistics.mean(v.values()) for c, v in ctrs.items()}
+    res = {"source_sha": source_sha(), "kernels": summary}
+    if calib_path:
+        res["copy_calibration"] = calib_path
+    with open(out_path, "w") as fh:
+        json.dump(res, fh, indent=1)
+    return res
+
+
+def load_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from committed counter summaries, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    if data.get("source_sha") != source_sha():
+        return None
+    scale = float(data.get("copy_scale", 1.0))
+    for name, ctr in data.get("kernels", {}).items():
+        if kernel in name and "FETCH_SIZE" in ctr and "WRITE_SIZE" in ctr:
+            return (ctr["FETCH_SIZE"] + ctr["WRITE_SIZE"]) * 1024.0 * scale
+    return None
+
+
+def copy_calibration(gib=1.0, reps=5):
+    import torch
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {n} bytes x {reps}")
+
+
+# --------------------------------------------------------------------------- main bench
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="mixtral_decode")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--rotations", type=int, default=0, help="weight-pool copies (0: enough to defeat the MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--pmc-out", metavar="JSON")
+    args = ap.parse_args(argv)
+
+    if args.summarize_pmc:
+        res = summarize_pmc(args.summarize_pmc, args.pmc_out or "pmc_summary.json")
+        print(json.dumps(res))
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this layer is built and measured on a single MI355X "
+              f"(--gpus {args.gpus} / WORLD_SIZE {world} is not supported)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from expert_ffn_layer_router_amd import DeviceWeights, MoeLayer, to_device
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    torch.cuda.set_device(0)
+    case = synth.make_case(args.config)
+    shape, w = case.shape, case.weights
+    log(f"workload {args.config}: T={shape.T} d={shape.d_model} d_ff={shape.d_ff} E={shape.num_experts} "
+        f"k={shape.top_k} slots={shape.num_slots}")
+
+    # routing of this batch (for the work accounting)
+    pool_bytes = w.nbytes()
+    T = shape.T
+    x = to_device(case.hidden).view(torch.bfloat16)
+    rw = to_device(w.router_w)
+    rb = None if w.router_b is None else to_device(w.router_b)
+    st = to_device(w.slot_table)
+    probe = MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T)
+    ws = probe.new_workspace(T)
+    out = torch.empty((T, shape.d_model), dtype=torch.bfloat16, device="cuda")
+
+    pools = [DeviceWeights.upload(w)]
+    probe.forward(x, rw, rb, st, pools[0], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    counts = probe.routing(ws, T)["counts"].cpu().numpy()
+    work = algorithmic_work(shape, counts)
+    active_bytes = work["layer"]["bytes"]
+    rot = args.rotations or max(2, -(-int(1.5 * MALL_BYTES) // max(1, active_bytes)) + 1)
+    rot = min(rot, max(1, int(60e9 // max(1, pool_bytes))))
+    for _ in range(rot - 1):
+        pools.append(DeviceWeights.upload(w))
+    log(f"{work['active']} active experts, {active_bytes / 1e6:.1f} MB algorithmic per step, "
+        f"{rot} weight-pool copies of {pool_bytes / 1e6:.1f} MB")
+
+    layers = [MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T)
+              for _ in range(rot)]
+    stream = torch.cuda.Stream()
+    if args.mode == "graph":
+        with torch.cuda.stream(stream):
+            for L, p in zip(layers, pools):
+                L.capture(x, rw, rb, st, p, out, ws, stream)
+        stream.synchronize()
+
+    def step(i):
+        if args.mode == "graph":
+            layers[i % rot].replay(stream)
+        else:
+            layers[i % rot].forward(x, rw, rb, st, pools[i % rot], out=out, workspace=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    stream.synchronize()
+    torch.cuda.synchronize()
+
+    # timed region: K whole-layer steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        ev1.record(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = 1e3 * wall / args.steps
+    value = T * args.steps / wall
+    log(f"{args.mode}: {ms_per_step * 1e3:.1f} us/step wall, {ev_ms / args.steps * 1e3:.1f} us/step events")
+
+    # kernel timing: HIP events recorded by the library between stages, on the
+    # stream the kernels run on (eager launches of the same steps)
+    for L in layers:
+        L.set_stage_timing(args.steps)
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            layers[i % rot].forward(x, rw, rb, st, pools[i % rot], out=out, workspace=ws, stream=stream)
+    stream.synchronize()
+    stage_sum = {}
+    n_fw = 0
+    for L in layers:
+        ms, n = L.stage_times()
+        n_fw += n
+        for key, v in ms.items():
+            stage_sum[key] = stage_sum.get(key, 0.0) + v
+        L.set_stage_timing(0)
+    stage_us = {key: 1e3 * v / max(1, n_fw) for key, v in stage_sum.items()}
+    log("stage us: " + ", ".join(f"{key} {v:.1f}" for key, v in stage_us.items()))
+
+    bound = DECODE_BOUND.get(args.config, "hbm")
+    dom = max(("gate_up", "down"), key=lambda s_: stage_us[s_])
+    dur_s = stage_us[dom] * 1e-6
+    if bound == "hbm":
+        achieved = work[dom]["bytes"] / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = work[dom]["flops"] / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS}
+    roof["kernel"] = KERNEL_OF_STAGE[dom]
+    roof["kernel_us"] = stage_us[dom]
+    roof["algorithmic_bytes"] = work[dom]["bytes"]
+    roof["algorithmic_flops"] = work[dom]["flops"]
+    roof["traffic"] = load_traffic(args.config, KERNEL_OF_STAGE[dom])
+
+    layer_s = ms_per_step * 1e-3
+    result = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.config, "T": T, "d_model": shape.d_model, "d_ff": shape.d_ff,
+                   "num_experts": shape.num_experts, "top_k": shape.top_k, "num_slots": shape.num_slots,
+                   "weights": "int4 codes + fp16 scale/zero-point per output row", "mode": args.mode,
+                   "weight_pool_copies": rot, "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"algorithmic_bytes": work["layer"]["bytes"], "algorithmic_flops": work["layer"]["flops"],
+                  "hbm_gbs": work["layer"]["bytes"] / layer_s / 1e9,
+                  "mfma_frac": work["layer"]["flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS,
+                  "active_experts": work["active"], "stage_us": stage_us,
+                  "event_us_per_step": 1e3 * ev_ms / args.steps},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

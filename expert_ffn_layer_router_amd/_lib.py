@@ -17,6 +17,8 @@ MOE_ERR_WORKSPACE_TOO_SMALL = 3
 MOE_ERR_HIP = 4
 MOE_ERR_BAD_STATE = 5
 MOE_FLAG_BAD_SLOT = 0x1
+MOE_NUM_STAGES = 5
+STAGE_NAMES = ("router", "regroup", "gate_up", "down", "combine")
 
 
 class MoeConfig(ctypes.Structure):
@@ -73,6 +75,8 @@ def load():
         "moe_graph_capture": (c_int, [vp, i32, vp, vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp, sz, vp]),
         "moe_graph_launch": (c_int, [vp, vp]),
         "moe_device_flags": (c_int, [vp, vp, i32, vp, ctypes.POINTER(ctypes.c_uint32)]),
+        "moe_set_stage_timing": (c_int, [vp, i32]),
+        "moe_stage_times": (c_int, [vp, ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]),
         "moe_status_string": (ctypes.c_char_p, [c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
     }

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_hip.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "moe_api.hip"]
+SOURCES = ["router.hip", "permute.hip", "grouped_gemm.hip", "stream_gemm.hip", "combine.hip", "moe_api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -49,25 +49,28 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, defines=(), out_path: str = LIB_PATH, build_dir: str = BUILD_DIR) -> str:
+    """Compiles every source and links `out_path`.  `defines` (e.g. "MOE_DOWN_NB=8")
+    override the tile-shape constants."""
+    os.makedirs(build_dir, exist_ok=True)
     hipcc = _hipcc()
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        out = _run([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+        out = _run([hipcc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
+                    "-o", obj])
         if verbose and out.strip():
             print(out)
         return obj
 
     with ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+    tmp = out_path + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out_path)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {out_path}")
+    return out_path
 
 
 if __name__ == "__main__":

@@ -83,4 +83,48 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// Hand-over between blocks of one kernel without flushing caches.  The L2 of
+// each XCD is not coherent with the others for ordinary accesses, and a
+// device-scope fence writes back and invalidates the whole L2.  Data that
+// the last block of a kernel reads from the other blocks is instead written
+// and read with device-scope relaxed atomics (coherent single accesses), the
+// writer waits for its stores to complete before taking its completion
+// ticket, and the ticket is a device-scope atomic counter.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(double* p, double v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), (uint64_t)__double_as_longlong(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double load_coherent(const double* p) {
+  return __longlong_as_double(
+      (long long)__hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<double*>(p)), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT));
+}
+// Waits until this thread's memory operations have completed (no cache flush).
+__device__ __forceinline__ void wait_all_memory() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Takes a completion ticket; true for the last of `total` blocks.  Every thread
+// of the block must call it (it contains barriers); the caller has stored its
+// hand-over data with store_coherent.
+__device__ __forceinline__ bool last_block_ticket(uint32_t* ticket, uint32_t total, int* lds_flag) {
+  wait_all_memory();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *lds_flag = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1;
+  __syncthreads();
+  const bool last = *lds_flag != 0;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return last;
+}
+__device__ __forceinline__ void reset_ticket(uint32_t* ticket) {
+  __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace moe

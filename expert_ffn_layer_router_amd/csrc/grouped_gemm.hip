@@ -30,9 +30,7 @@ constexpr int kMaxMB = kTileRows / 16;
 template <int NB>
 __global__ __launch_bounds__(256) void gateup_swiglu_kernel(
     const uint16_t* __restrict__ hidden, int d, int dff, int topk, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_e, const int32_t* __restrict__ tile_r0,
-    const int32_t* __restrict__ num_tiles, const int32_t* __restrict__ slot_table, int num_slots,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int num_slots,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, const uint16_t* __restrict__ sg,
     const uint16_t* __restrict__ zg, const uint16_t* __restrict__ su, const uint16_t* __restrict__ zu,
     uint16_t* __restrict__ h, uint32_t* __restrict__ flags) {
@@ -41,10 +39,8 @@ __global__ __launch_bounds__(256) void gateup_swiglu_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, grp = lane >> 4;
   const int n0 = (blockIdx.x * 4 + wave) * (16 * NB);
-  const int e = tile_e[tile], r0 = tile_r0[tile];
-  const int rows = min(kTileRows, counts[e] - r0);
-  const int pbase = offsets[e] + r0;
-  const int slot = slot_table[e];
+  const int4 td = tiles[tile];  // (expert, slot, first grouped row, rows)
+  const int slot = td.y, pbase = td.z, rows = td.w;
   if (slot < 0 || slot >= num_slots) {
     if (threadIdx.x == 0) atomicOr(flags, MOE_FLAG_BAD_SLOT);
     return;
@@ -148,10 +144,8 @@ __global__ __launch_bounds__(256) void gateup_swiglu_kernel(
 // ypart[split][p] = h[p] Wd^T over the k-range of `split` (fp32).
 template <int NB>
 __global__ __launch_bounds__(256) void down_kernel(
-    const uint16_t* __restrict__ h, int d, int dff, int kchunk, int R, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_e,
-    const int32_t* __restrict__ tile_r0, const int32_t* __restrict__ num_tiles,
-    const int32_t* __restrict__ slot_table, int num_slots, const uint8_t* __restrict__ wd,
+    const uint16_t* __restrict__ h, int d, int dff, int kchunk, int R, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, int num_slots, const uint8_t* __restrict__ wd,
     const uint16_t* __restrict__ sd, const uint16_t* __restrict__ zd, float* __restrict__ ypart,
     uint32_t* __restrict__ flags) {
   const int tile = blockIdx.y;
@@ -161,10 +155,8 @@ __global__ __launch_bounds__(256) void down_kernel(
   const int n0 = (blockIdx.x * 4 + wave) * (16 * NB);
   const int split = blockIdx.z;
   const int kbeg = split * kchunk;
-  const int e = tile_e[tile], r0 = tile_r0[tile];
-  const int rows = min(kTileRows, counts[e] - r0);
-  const int pbase = offsets[e] + r0;
-  const int slot = slot_table[e];
+  const int4 td = tiles[tile];  // (expert, slot, first grouped row, rows)
+  const int slot = td.y, pbase = td.z, rows = td.w;
   const int nmb = (rows + 15) >> 4;
   float* yrow = ypart + ((size_t)split * R + pbase) * d;
 
@@ -249,28 +241,31 @@ __global__ __launch_bounds__(256) void down_kernel(
   }
 }
 
-void launch_gemms(const moe_config& c, const Plan& p, const uint16_t* hidden, const int32_t* slot_table,
-                  const moe_weights& w, char* ws, hipStream_t s) {
-  constexpr int NB = 2;  // 4 waves x 2 x 16 = kGemmColsPerBlock columns per block
-  const int32_t* counts = reinterpret_cast<const int32_t*>(ws + p.counts);
-  const int32_t* offsets = reinterpret_cast<const int32_t*>(ws + p.offsets);
-  const int32_t* perm = reinterpret_cast<const int32_t*>(ws + p.perm);
-  const int32_t* tile_e = reinterpret_cast<const int32_t*>(ws + p.tile_e);
-  const int32_t* tile_r0 = reinterpret_cast<const int32_t*>(ws + p.tile_r0);
-  const int32_t* num_tiles = reinterpret_cast<const int32_t*>(ws + p.num_tiles);
-  uint16_t* h = reinterpret_cast<uint16_t*>(ws + p.h);
-  float* y = reinterpret_cast<float*>(ws + p.y);
-  uint32_t* flags = reinterpret_cast<uint32_t*>(ws + p.flags);
+namespace {
+constexpr int kNB = 2;  // generic family: 4 waves x kNB x 16 = kGemmColsPerBlock columns per block
+}  // namespace
 
-  dim3 g1(c.d_ff / kGemmColsPerBlock, p.max_tiles, 1);
-  gateup_swiglu_kernel<NB><<<g1, 256, 0, s>>>(hidden, c.d_model, c.d_ff, c.top_k, perm, counts, offsets,
-                                              tile_e, tile_r0, num_tiles, slot_table, c.num_slots,
-                                              w.w_gate, w.w_up, w.s_gate, w.z_gate, w.s_up, w.z_up, h,
-                                              flags);
-  dim3 g2(c.d_model / kGemmColsPerBlock, p.max_tiles, p.down_split);
-  down_kernel<NB><<<g2, 256, 0, s>>>(h, c.d_model, c.d_ff, c.d_ff / p.down_split, p.R, counts, offsets,
-                                     tile_e, tile_r0, num_tiles, slot_table, c.num_slots, w.w_down,
-                                     w.s_down, w.z_down, y, flags);
+void launch_gateup(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w, char* ws,
+                   hipStream_t s) {
+  if (p.family == GemmFamily::kStream) return launch_gateup_stream(c, p, hidden, w, ws, s);
+  dim3 grid(c.d_ff / kGemmColsPerBlock, p.max_tiles, 1);
+  gateup_swiglu_kernel<kNB><<<grid, 256, 0, s>>>(
+      hidden, c.d_model, c.d_ff, c.top_k, reinterpret_cast<const int32_t*>(ws + p.perm),
+      reinterpret_cast<const int4*>(ws + p.tiles), reinterpret_cast<const int32_t*>(ws + p.num_tiles),
+      c.num_slots, w.w_gate, w.w_up,
+      w.s_gate, w.z_gate, w.s_up, w.z_up, reinterpret_cast<uint16_t*>(ws + p.h),
+      reinterpret_cast<uint32_t*>(ws + p.flags));
+}
+
+void launch_down(const moe_config& c, const Plan& p, const moe_weights& w, uint16_t* out, char* ws,
+                 hipStream_t s) {
+  if (p.family == GemmFamily::kStream) return launch_down_stream(c, p, w, out, ws, s);
+  dim3 grid(c.d_model / kGemmColsPerBlock, p.max_tiles, p.down_split);
+  down_kernel<kNB><<<grid, 256, 0, s>>>(
+      reinterpret_cast<const uint16_t*>(ws + p.h), c.d_model, c.d_ff, c.d_ff / p.down_split, p.R,
+      reinterpret_cast<const int4*>(ws + p.tiles), reinterpret_cast<const int32_t*>(ws + p.num_tiles),
+      c.num_slots, w.w_down, w.s_down,
+      w.z_down, reinterpret_cast<float*>(ws + p.y), reinterpret_cast<uint32_t*>(ws + p.flags));
 }
 
 }  // namespace moe

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "moe.h"
 #include "plan.h"
@@ -47,6 +48,10 @@ struct moe_layer {
   moe_config cfg{};
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  // stage timing: (MOE_NUM_STAGES + 1) events per recorded forward
+  std::vector<hipEvent_t> events;
+  int timing_capacity = 0;
+  int timing_recorded = 0;
 };
 
 namespace moe {
@@ -56,15 +61,33 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   p->T = T;
   p->R = T * c.top_k;
   const int E = c.num_experts;
-  // router: enough blocks to cover the chip when T is small
-  const int chunks = c.d_model / kRouterKChunk;
-  const int router_blocks = ((T + kRouterTokTile - 1) / kRouterTokTile) * ((E + kRouterExpTile - 1) / kRouterExpTile);
-  p->router_split = largest_divisor_at_most(chunks, std::max(1, 512 / std::max(1, router_blocks)));
+  if (T <= kStreamMaxTokens) {
+    p->family = GemmFamily::kStream;
+    p->tile_rows = T <= 16 ? 16 : 32;
+  } else {
+    p->family = GemmFamily::kGeneric;
+    p->tile_rows = kTileRows;
+  }
+  p->fused_small = T <= kStreamMaxTokens;
+  if (T <= kStreamMaxTokens) {
+    p->router_split = 0;
+  } else {
+    // 64 x 64 tiles; split k (in multiples of 32) until about 256 blocks
+    const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
+    p->router_split = largest_divisor_at_most(c.d_model / 32, std::max(1, (256 + tiles - 1) / tiles));
+  }
   // GEMM row tiles: sum_e ceil(c_e / rows) <= ceil(R / rows) + (non-empty experts)
-  p->max_tiles = (p->R + kTileRows - 1) / kTileRows + std::min(E, p->R);
-  // split the down projection's k range until ~4 blocks per compute unit
-  const int down_blocks = std::max(1, p->max_tiles * (c.d_model / kGemmColsPerBlock));
-  p->down_split = largest_divisor_at_most(c.d_ff / kGemmKStep, (1024 + down_blocks - 1) / down_blocks);
+  p->max_tiles = (p->R + p->tile_rows - 1) / p->tile_rows + std::min(E, p->R);
+  // split the down projection's k range until the grid has enough blocks
+  if (p->family == GemmFamily::kStream) {
+    p->gateup_ncw = (kStreamMaxNCW >= 2 && c.d_ff % 128 == 0) ? 2 : 1;
+    p->down_ncw = (kStreamMaxNCW >= 2 && c.d_model % 128 == 0) ? 2 : 1;
+    const int blocks = std::max(1, p->max_tiles * (c.d_model / (64 * p->down_ncw)));
+    p->down_split = largest_divisor_at_most(c.d_ff / kGemmKStep, (kDownStreamBlocks + blocks - 1) / blocks);
+  } else {
+    const int blocks = std::max(1, p->max_tiles * (c.d_model / kGemmColsPerBlock));
+    p->down_split = largest_divisor_at_most(c.d_ff / kGemmKStep, (1024 + blocks - 1) / blocks);
+  }
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -73,16 +96,18 @@ void make_plan(const moe_config& c, int T, Plan* p) {
     return at;
   };
   const size_t R = (size_t)p->R;
+  // control words: [0] router ticket, [1 + i] combine ticket of output column slice i
+  p->ctrl = take(4 * (1 + (size_t)c.d_model / kStreamCols));
+  p->ctrl_bytes = off;  // aligned end of the control words (they start at offset 0)
   p->flags = take(4);
-  p->logit_part = take(sizeof(double) * (size_t)p->router_split * T * E);
+  p->logits = take(sizeof(double) * (size_t)std::max(1, p->router_split) * T * E);
   p->topk_idx = take(4 * R);
   p->topk_w = take(4 * R);
   p->counts = take(4 * (size_t)E);
   p->offsets = take(4 * (size_t)(E + 1));
   p->perm = take(4 * R);
   p->inv = take(4 * R);
-  p->tile_e = take(4 * (size_t)p->max_tiles);
-  p->tile_r0 = take(4 * (size_t)p->max_tiles);
+  p->tiles = take(16 * (size_t)p->max_tiles);
   p->num_tiles = take(4);
   p->h = take(2 * R * (size_t)c.d_ff);
   p->y = take(4 * (size_t)p->down_split * R * (size_t)c.d_model);
@@ -132,17 +157,38 @@ moe_status check_forward_args(moe_handle h, int32_t T, const uint16_t* hidden, c
   return MOE_OK;
 }
 
-moe_status enqueue(const moe_layer* h, const moe::Plan& p, const uint16_t* hidden, const float* router_w,
+moe_status enqueue(moe_layer* h, const moe::Plan& p, const uint16_t* hidden, const float* router_w,
                    const float* router_bias, const int32_t* slot_table, const moe_weights* w, uint16_t* out,
-                   void* workspace, hipStream_t s) {
+                   void* workspace, hipStream_t s, bool capturing) {
   char* ws = static_cast<char*>(workspace);
-  moe::launch_router(h->cfg, p, hidden, router_w, router_bias, ws, s);
-  moe::launch_permute(h->cfg, p, ws, s);
-  moe::launch_gemms(h->cfg, p, hidden, slot_table, *w, ws, s);
-  moe::launch_combine(h->cfg, p, out, ws, s);
+  hipEvent_t* ev = nullptr;
+  if (!capturing && h->timing_recorded < h->timing_capacity)
+    ev = &h->events[(size_t)h->timing_recorded++ * (MOE_NUM_STAGES + 1)];
+  auto mark = [&](int i) {
+    if (ev) (void)hipEventRecord(ev[i], s);
+  };
+  // with few tokens the regroup runs inside the router kernel and the
+  // combine inside the down kernel (their stages then time as empty)
+  mark(0);
+  moe::launch_router(h->cfg, p, hidden, router_w, router_bias, slot_table, ws, s);
+  mark(1);
+  if (!p.fused_small) moe::launch_permute(h->cfg, p, slot_table, ws, s);
+  mark(2);
+  moe::launch_gateup(h->cfg, p, hidden, *w, ws, s);
+  mark(3);
+  moe::launch_down(h->cfg, p, *w, out, ws, s);
+  mark(4);
+  if (!p.fused_small) moe::launch_combine(h->cfg, p, out, ws, s);
+  mark(5);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return MOE_OK;
+}
+
+void drop_events(moe_layer* h) {
+  for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+  h->events.clear();
+  h->timing_capacity = h->timing_recorded = 0;
 }
 
 void drop_graph(moe_layer* h) {
@@ -180,6 +226,7 @@ MOE_EXPORT moe_status moe_create(const moe_config* cfg, moe_handle* out) {
 MOE_EXPORT void moe_destroy(moe_handle h) {
   if (!h || h->magic != kMagic) return;
   drop_graph(h);
+  drop_events(h);
   h->magic = 0;
   delete h;
 }
@@ -203,7 +250,7 @@ MOE_EXPORT moe_status moe_forward(moe_handle h, int32_t T, const uint16_t* hidde
                                      workspace_bytes, &p);
   if (st != MOE_OK || T == 0) return st;
   return enqueue(h, p, hidden, router_w, router_bias, slot_table, w, out, workspace,
-                 static_cast<hipStream_t>(stream));
+                 static_cast<hipStream_t>(stream), false);
 }
 
 MOE_EXPORT moe_status moe_routing_view(moe_handle h, const void* workspace, int32_t T, moe_routing* view) {
@@ -237,7 +284,7 @@ MOE_EXPORT moe_status moe_graph_capture(moe_handle h, int32_t T, const uint16_t*
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
   if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(err));
-  const moe_status est = enqueue(h, p, hidden, router_w, router_bias, slot_table, w, out, workspace, s);
+  const moe_status est = enqueue(h, p, hidden, router_w, router_bias, slot_table, w, out, workspace, s, true);
   hipGraph_t graph = nullptr;
   err = hipStreamEndCapture(s, &graph);
   if (est != MOE_OK) {
@@ -280,6 +327,51 @@ MOE_EXPORT moe_status moe_device_flags(moe_handle h, const void* workspace, int3
   if (err == hipSuccess) err = hipStreamSynchronize(s);
   if (err != hipSuccess) return fail(MOE_ERR_HIP, "reading device flags: %s", hipGetErrorString(err));
   *flags = v;
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_set_stage_timing(moe_handle h, int32_t max_forwards) {
+  moe_status st = check_handle(h);
+  if (st != MOE_OK) return st;
+  if (max_forwards < 0 || max_forwards > 100000)
+    return fail(MOE_ERR_INVALID_ARG, "max_forwards=%d outside [0, 100000]", max_forwards);
+  drop_events(h);
+  const size_t n = (size_t)max_forwards * (MOE_NUM_STAGES + 1);
+  h->events.reserve(n);
+  for (size_t i = 0; i < n; ++i) {
+    hipEvent_t e = nullptr;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      drop_events(h);
+      return fail(MOE_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(err));
+    }
+    h->events.push_back(e);
+  }
+  h->timing_capacity = max_forwards;
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_stage_times(moe_handle h, float* ms, int32_t n_stages, int32_t* forwards) {
+  moe_status st = check_handle(h);
+  if (st != MOE_OK) return st;
+  if (!ms || !forwards) return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  if (n_stages < MOE_NUM_STAGES) return fail(MOE_ERR_INVALID_ARG, "n_stages=%d < %d", n_stages, MOE_NUM_STAGES);
+  for (int i = 0; i < MOE_NUM_STAGES; ++i) ms[i] = 0.0f;
+  const int n = h->timing_recorded;
+  if (n > 0) {
+    hipError_t err = hipEventSynchronize(h->events[(size_t)n * (MOE_NUM_STAGES + 1) - 1]);
+    for (int f = 0; f < n && err == hipSuccess; ++f) {
+      const hipEvent_t* ev = &h->events[(size_t)f * (MOE_NUM_STAGES + 1)];
+      for (int i = 0; i < MOE_NUM_STAGES && err == hipSuccess; ++i) {
+        float t = 0.0f;
+        err = hipEventElapsedTime(&t, ev[i], ev[i + 1]);
+        ms[i] += t;
+      }
+    }
+    if (err != hipSuccess) return fail(MOE_ERR_HIP, "reading stage events: %s", hipGetErrorString(err));
+  }
+  *forwards = n;
+  h->timing_recorded = 0;
   return MOE_OK;
 }
 

@@ -11,33 +11,63 @@
 
 namespace moe {
 
-constexpr int kRouterTokTile = 16;     // tokens per router block
-constexpr int kRouterExpTile = 64;     // experts per router block
-constexpr int kRouterKChunk = 64;      // k per router LDS stage
-constexpr int kTileRows = 64;          // rows of an expert group per GEMM tile
-constexpr int kGemmColsPerBlock = 128; // output columns per GEMM block (4 waves x 32)
+constexpr int kRouterTokTile = 16;     // tokens per router wave
+constexpr int kTileRows = 64;          // rows of an expert group per generic-family GEMM tile
+constexpr int kGemmColsPerBlock = 128; // output columns per generic-family GEMM block (4 waves x 32)
 constexpr int kGemmKStep = 128;        // k per GEMM load step
 constexpr int kPermuteThreads = 1024;
+constexpr int kStreamMaxTokens = 64;   // up to this T the decode (weight-streaming) family runs
+
+#ifndef MOE_DOWN_BLOCKS
+#define MOE_DOWN_BLOCKS 2048
+#endif
+#ifndef MOE_STREAM_NCW
+#define MOE_STREAM_NCW 1
+#endif
+#ifndef MOE_STREAM_BUFFERS
+#define MOE_STREAM_BUFFERS 2
+#endif
+constexpr int kStreamCols = 64;                     // decode family: narrowest block (64 output columns)
+constexpr int kStreamMaxNCW = MOE_STREAM_NCW;       // decode family: widest block, 64 x this many columns
+constexpr int kStreamBuffers = MOE_STREAM_BUFFERS;  // decode family: LDS stage buffers (stages in flight + 1)
+constexpr int kDownStreamBlocks = MOE_DOWN_BLOCKS;  // k-split the decode down GEMM up to about this many blocks
+
+enum class GemmFamily { kStream, kGeneric };
 
 struct Plan {
   int T = 0, R = 0;
-  int router_split = 1;   // k-split of the router GEMV
-  int down_split = 1;     // k-split of the down projection
-  int max_tiles = 0;      // upper bound on GEMM row tiles
-  // byte offsets into the workspace
-  size_t flags = 0, logit_part = 0, topk_idx = 0, topk_w = 0, counts = 0, offsets = 0,
-         perm = 0, inv = 0, tile_e = 0, tile_r0 = 0, num_tiles = 0, h = 0, y = 0, total = 0;
+  GemmFamily family = GemmFamily::kGeneric;
+  int router_split = 0;       // 0: few-token router; else k-splits of the tiled router
+  int gateup_ncw = 1, down_ncw = 1;  // decode family: blocks of 64 x ncw output columns
+  int tile_rows = kTileRows;  // rows of an expert group per GEMM row tile
+  int down_split = 1;         // k-split of the down projection
+  int max_tiles = 0;          // upper bound on GEMM row tiles
+  bool fused_small = false;   // few tokens: router + top-k + regroup in one kernel, combine fused into down
+  // byte offsets into the workspace; [ctrl, ctrl + ctrl_bytes) are control
+  // words that must be zero before first use and are left zero by every call
+  size_t ctrl = 0, ctrl_bytes = 0, flags = 0, logits = 0, topk_idx = 0, topk_w = 0, counts = 0,
+         offsets = 0, perm = 0, inv = 0, tiles = 0, num_tiles = 0, h = 0, y = 0, total = 0;
 };
 
 // Fills `p` for T tokens.  Pure host arithmetic.
 void make_plan(const moe_config& c, int T, Plan* p);
 
+struct RegroupArgs;
+RegroupArgs regroup_args(const moe_config& c, const Plan& p, const int32_t* slot_table, char* ws);
+
 // Kernel launchers (enqueue only).
 void launch_router(const moe_config& c, const Plan& p, const uint16_t* hidden, const float* router_w,
-                   const float* router_bias, char* ws, hipStream_t s);
-void launch_permute(const moe_config& c, const Plan& p, char* ws, hipStream_t s);
-void launch_gemms(const moe_config& c, const Plan& p, const uint16_t* hidden, const int32_t* slot_table,
-                  const moe_weights& w, char* ws, hipStream_t s);
+                   const float* router_bias, const int32_t* slot_table, char* ws, hipStream_t s);
+void launch_permute(const moe_config& c, const Plan& p, const int32_t* slot_table, char* ws, hipStream_t s);
+void launch_gateup(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w, char* ws,
+                   hipStream_t s);
+void launch_down(const moe_config& c, const Plan& p, const moe_weights& w, uint16_t* out, char* ws,
+                 hipStream_t s);
+// decode family (stream_gemm.hip); with p.fused_small the down launch also writes out
+void launch_gateup_stream(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w,
+                          char* ws, hipStream_t s);
+void launch_down_stream(const moe_config& c, const Plan& p, const moe_weights& w, uint16_t* out, char* ws,
+                        hipStream_t s);
 void launch_combine(const moe_config& c, const Plan& p, uint16_t* out, char* ws, hipStream_t s);
 
 }  // namespace moe

@@ -8,117 +8,237 @@
 // through the same sequence of operations.
 #include "device_common.h"
 #include "plan.h"
+#include "regroup.h"
 
 namespace moe {
 
-// Partial logits over one k-range: part[split][t][e] (fp64).
-// Block: 16 tokens x 64 experts; thread (ty, tx) owns token ty and experts
-// tx, tx+16, tx+32, tx+48.
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ hidden,
-                                                            const float* __restrict__ wr,
-                                                            double* __restrict__ part, int T, int d,
-                                                            int E, int kchunk) {
-  __shared__ float xs[kRouterTokTile][kRouterKChunk + 1];
-  __shared__ float ws[kRouterExpTile][kRouterKChunk + 1];
-  const int t0 = blockIdx.x * kRouterTokTile;
-  const int e0 = blockIdx.y * kRouterExpTile;
-  const int split = blockIdx.z;
-  const int kbeg = split * kchunk;
-  const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int kc = kbeg; kc < kbeg + kchunk; kc += kRouterKChunk) {
-    for (int i = tid; i < kRouterTokTile * kRouterKChunk; i += 256) {
-      const int r = i / kRouterKChunk, c = i % kRouterKChunk;
-      const int t = t0 + r;
-      xs[r][c] = (t < T) ? bf16_to_f32(hidden[(size_t)t * d + kc + c]) : 0.0f;
-    }
-    for (int i = tid; i < kRouterExpTile * kRouterKChunk; i += 256) {
-      const int r = i / kRouterKChunk, c = i % kRouterKChunk;
-      const int e = e0 + r;
-      ws[r][c] = (e < E) ? wr[(size_t)e * d + kc + c] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int c = 0; c < kRouterKChunk; ++c) {
-      const double xv = xs[ty][c];
+// Top-k of one token, run by one wave: add the bias to the (split-summed)
+// logits, then k rounds of a wave-wide arg-max over the experts not yet
+// chosen (largest logit, ties to the lower id), then
+// w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+template <bool kCoherent>
+__device__ void topk_token(const double* __restrict__ logits, int nsplit, const float* __restrict__ bias, int T,
+                           int E, int k, int t, int lane, int32_t* __restrict__ topk_idx,
+                           float* __restrict__ topk_w) {
+  constexpr int kPer = 4;  // experts per lane: E <= 256
+  double l[kPer];
+  bool live[kPer];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = fma(xv, (double)ws[tx + 16 * j][c], acc[j]);
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + 64 * j;
+    live[j] = e < E;
+    double v = 0.0;
+    if (live[j]) {
+      if (kCoherent) {
+        v = load_coherent(&logits[(size_t)t * E + e]);
+      } else {
+        v = logits[(size_t)t * E + e];
+        for (int s = 1; s < nsplit; ++s) v += logits[((size_t)s * T + t) * E + e];
+      }
+      if (bias) v += (double)bias[e];
     }
-    __syncthreads();
+    l[j] = v;
   }
-  const int t = t0 + ty;
-  if (t < T) {
+  double best[8];
+  int bid[8];
+  for (int r = 0; r < k; ++r) {
+    // this lane's best: largest value, lowest id (ids ascend with j)
+    double v = 0.0;
+    int id = 0x7fffffff;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx + 16 * j;
-      if (e < E) part[((size_t)split * T + t) * E + e] = acc[j];
+    for (int j = 0; j < kPer; ++j) {
+      if (live[j] && (id == 0x7fffffff || l[j] > v)) {
+        v = l[j];
+        id = lane + 64 * j;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(v, off, 64);
+      const int oid = __shfl_xor(id, off, 64);
+      const bool take = (oid != 0x7fffffff) && (id == 0x7fffffff || ov > v || (ov == v && oid < id));
+      if (take) {
+        v = ov;
+        id = oid;
+      }
+    }
+    best[r] = v;
+    bid[r] = id;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (lane + 64 * j == id) live[j] = false;
+  }
+  if (lane == 0) {
+    double ex[8], den = 0.0;
+    for (int j = 0; j < k; ++j) {
+      ex[j] = exp(best[j] - best[0]);
+      den += ex[j];
+    }
+    for (int j = 0; j < k; ++j) {
+      topk_idx[(size_t)t * k + j] = bid[j];
+      topk_w[(size_t)t * k + j] = (float)(ex[j] / den);
     }
   }
 }
 
-// One thread per token: sum the partial logits in split order, add the bias,
-// keep the k largest (strictly larger replaces, so the earlier, lower id wins
-// a tie), then w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
-// Also clears the device error flags of this forward.
-__global__ __launch_bounds__(256) void router_topk_kernel(const double* __restrict__ part, int nsplit,
+// Few tokens (T <= kStreamMaxTokens): one block per (expert, group of
+// kRouterTokTile tokens); its 4 waves take a quarter of d each, lane l
+// accumulating k = 8l .. 8l+7 of every 512 for all tokens of the group; a
+// butterfly over the lanes and a fixed-order sum over the 4 waves (through
+// LDS) finish each logit.  The last block to finish (an atomic ticket in the
+// workspace's control words) then runs the top-k of every token and the
+// regroup, and clears the ticket for the next call.
+__global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ hidden,
+                                                           const float* __restrict__ wr,
+                                                           const float* __restrict__ bias,
+                                                           double* __restrict__ logits, int T, int d, int E,
+                                                           int k, int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_w,
+                                                           uint32_t* __restrict__ flags,
+                                                           uint32_t* __restrict__ ticket, RegroupArgs ra) {
+  __shared__ double part[4][kRouterTokTile];
+  __shared__ int is_last;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.x;
+  const int t0 = blockIdx.y * kRouterTokTile;
+  const int nt = min(kRouterTokTile, T - t0);
+  double acc[kRouterTokTile];
+#pragma unroll
+  for (int t = 0; t < kRouterTokTile; ++t) acc[t] = 0.0;
+  const int kq = d / 4;
+  const int kend = (wave + 1) * kq;
+  const float* wrow = wr + (size_t)e * d;
+  for (int kk = wave * kq + lane * 8; kk < kend; kk += 512) {
+    const float4 w0 = *reinterpret_cast<const float4*>(wrow + kk);
+    const float4 w1 = *reinterpret_cast<const float4*>(wrow + kk + 4);
+    const double wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    u32x4 xv[kRouterTokTile];
+#pragma unroll
+    for (int t = 0; t < kRouterTokTile; ++t)  // rows past T re-read the group's first row
+      xv[t] = *reinterpret_cast<const u32x4*>(hidden + (size_t)(t0 + (t < nt ? t : 0)) * d + kk);
+#pragma unroll
+    for (int t = 0; t < kRouterTokTile; ++t) {
+      const uint32_t xs[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[t] = fma((double)__uint_as_float(xs[i] << 16), wv[2 * i], acc[t]);
+        acc[t] = fma((double)__uint_as_float(xs[i] & 0xFFFF0000u), wv[2 * i + 1], acc[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kRouterTokTile; ++t) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc[t] += __shfl_xor(acc[t], off, 64);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int t = 0; t < kRouterTokTile; ++t) part[wave][t] = acc[t];
+  }
+  __syncthreads();
+  if (wave == 0 && lane < nt) {
+    const double v = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    store_coherent(&logits[(size_t)(t0 + lane) * E + e], v);
+  }
+  // the last block to finish reads every block's logits
+  if (!last_block_ticket(ticket, gridDim.x * gridDim.y, &is_last)) return;
+  if (threadIdx.x == 0) *flags = 0u;
+  for (int t = wave; t < T; t += 4) topk_token<true>(logits, 1, bias, T, E, k, t, lane, topk_idx, topk_w);
+  __syncthreads();
+  regroup_block<256>(ra);
+  if (threadIdx.x == 0) reset_ticket(ticket);
+}
+
+// Many tokens: an fp64 GEMM tile of 64 tokens x 64 experts per block over one
+// k-split; operands are widened to fp64 once, in LDS, and every thread owns a
+// 4 x 4 block of logits.  Output: logits[split][t][e], summed in split order
+// by router_topk_kernel.
+constexpr int kRtTok = 64, kRtExp = 64, kRtK = 32;
+__global__ __launch_bounds__(256) void router_logits_tiled_kernel(const uint16_t* __restrict__ hidden,
+                                                                  const float* __restrict__ wr,
+                                                                  double* __restrict__ logits, int T, int d,
+                                                                  int E, int kchunk) {
+  __shared__ double xs[kRtK][kRtTok];
+  __shared__ double ws[kRtK][kRtExp];
+  const int tid = threadIdx.x;
+  const int ty = tid >> 4, tx = tid & 15;  // tokens 4ty.., experts 4tx..
+  const int t0 = blockIdx.x * kRtTok, e0 = blockIdx.y * kRtExp, split = blockIdx.z;
+  const int kbeg = split * kchunk;
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int kc = kbeg; kc < kbeg + kchunk; kc += kRtK) {
+    for (int i = tid; i < kRtTok * kRtK; i += 256) {
+      const int r = i / kRtK, c = i % kRtK;
+      const int t = t0 + r;
+      xs[c][r] = (t < T) ? (double)bf16_to_f32(hidden[(size_t)t * d + kc + c]) : 0.0;
+    }
+    for (int i = tid; i < kRtExp * kRtK; i += 256) {
+      const int r = i / kRtK, c = i % kRtK;
+      const int e = e0 + r;
+      ws[c][r] = (e < E) ? (double)wr[(size_t)e * d + kc + c] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = 0; c < kRtK; ++c) {
+      double a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = xs[c][4 * ty + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = ws[c][4 * tx + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * ty + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + 4 * tx + j;
+      if (e < E) logits[((size_t)split * T + t) * E + e] = acc[i][j];
+    }
+  }
+}
+
+// One wave per token (many-token path).  Also clears the device error flags
+// of this forward.
+__global__ __launch_bounds__(256) void router_topk_kernel(const double* __restrict__ logits, int nsplit,
                                                           const float* __restrict__ bias, int T, int E,
                                                           int k, int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ topk_w,
                                                           uint32_t* __restrict__ flags) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  double best[8];
-  int bid[8];
-  int n = 0;
-  for (int e = 0; e < E; ++e) {
-    double l = part[(size_t)t * E + e];
-    for (int s = 1; s < nsplit; ++s) l += part[((size_t)s * T + t) * E + e];
-    if (bias) l += (double)bias[e];
-    if (n < k) {
-      int i = n++;
-      while (i > 0 && best[i - 1] < l) {
-        best[i] = best[i - 1];
-        bid[i] = bid[i - 1];
-        --i;
-      }
-      best[i] = l;
-      bid[i] = e;
-    } else if (l > best[k - 1]) {
-      int i = k - 1;
-      while (i > 0 && best[i - 1] < l) {
-        best[i] = best[i - 1];
-        bid[i] = bid[i - 1];
-        --i;
-      }
-      best[i] = l;
-      bid[i] = e;
-    }
-  }
-  double den = 0.0;
-  double ex[8];
-  for (int j = 0; j < k; ++j) {
-    ex[j] = exp(best[j] - best[0]);
-    den += ex[j];
-  }
-  for (int j = 0; j < k; ++j) {
-    topk_idx[(size_t)t * k + j] = bid[j];
-    topk_w[(size_t)t * k + j] = (float)(ex[j] / den);
-  }
+  topk_token<false>(logits, nsplit, bias, T, E, k, t, threadIdx.x & 63, topk_idx, topk_w);
 }
 
 void launch_router(const moe_config& c, const Plan& p, const uint16_t* hidden, const float* router_w,
-                   const float* router_bias, char* ws, hipStream_t s) {
-  double* part = reinterpret_cast<double*>(ws + p.logit_part);
-  dim3 grid((p.T + kRouterTokTile - 1) / kRouterTokTile, (c.num_experts + kRouterExpTile - 1) / kRouterExpTile,
-            p.router_split);
-  router_logits_kernel<<<grid, 256, 0, s>>>(hidden, router_w, part, p.T, c.d_model, c.num_experts,
-                                            c.d_model / p.router_split);
-  router_topk_kernel<<<(p.T + 255) / 256, 256, 0, s>>>(
-      part, p.router_split, router_bias, p.T, c.num_experts, c.top_k,
-      reinterpret_cast<int32_t*>(ws + p.topk_idx), reinterpret_cast<float*>(ws + p.topk_w),
-      reinterpret_cast<uint32_t*>(ws + p.flags));
+                   const float* router_bias, const int32_t* slot_table, char* ws, hipStream_t s) {
+  double* logits = reinterpret_cast<double*>(ws + p.logits);
+  int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + p.topk_idx);
+  float* topk_w = reinterpret_cast<float*>(ws + p.topk_w);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(ws + p.flags);
+  if (p.fused_small) {
+    dim3 grid(c.num_experts, (p.T + kRouterTokTile - 1) / kRouterTokTile);
+    router_small_kernel<<<grid, 256, 0, s>>>(hidden, router_w, router_bias, logits, p.T, c.d_model,
+                                             c.num_experts, c.top_k, topk_idx, topk_w, flags,
+                                             reinterpret_cast<uint32_t*>(ws + p.ctrl),
+                                             regroup_args(c, p, slot_table, ws));
+    return;
+  }
+  dim3 grid((p.T + kRtTok - 1) / kRtTok, (c.num_experts + kRtExp - 1) / kRtExp, p.router_split);
+  router_logits_tiled_kernel<<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, c.num_experts,
+                                                  c.d_model / p.router_split);
+  router_topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(logits, p.router_split, router_bias, p.T, c.num_experts,
+                                                   c.top_k, topk_idx, topk_w, flags);
 }
 
 }  // namespace moe

@@ -76,8 +76,9 @@ class MoeLayer:
         return n.value
 
     def new_workspace(self, T: int, device="cuda"):
+        """A zero-filled workspace (the library's control words must start at zero)."""
         torch = _torch()
-        return torch.empty(max(self.workspace_size(T), 256), dtype=torch.uint8, device=device)
+        return torch.zeros(max(self.workspace_size(T), 256), dtype=torch.uint8, device=device)
 
     @staticmethod
     def _stream(stream):
@@ -132,6 +133,16 @@ class MoeLayer:
                     offsets=view(v.offsets, E + 1, torch.int32),
                     perm=view(v.perm, R, torch.int32),
                     inv_perm=view(v.inv_perm, R, torch.int32))
+
+    def set_stage_timing(self, max_forwards: int) -> None:
+        _lib.check(self.lib.moe_set_stage_timing(self.handle, int(max_forwards)))
+
+    def stage_times(self):
+        """(summed ms per stage as a dict, number of forwards) since the last call."""
+        ms = (ctypes.c_float * _lib.MOE_NUM_STAGES)()
+        n = ctypes.c_int32()
+        _lib.check(self.lib.moe_stage_times(self.handle, ms, _lib.MOE_NUM_STAGES, ctypes.byref(n)))
+        return dict(zip(_lib.STAGE_NAMES, [float(v) for v in ms])), int(n.value)
 
     def device_flags(self, workspace, T: int, stream=None) -> int:
         f = ctypes.c_uint32()

@@ -30,6 +30,9 @@
  *   - Device pointers are caller-owned, must be 16-byte aligned, and must stay
  *     valid until the enqueued work completes.  The library allocates no
  *     device memory; all intermediates live in the caller's workspace.
+ *   - A workspace must be zero-filled once before its first use.  Its first
+ *     bytes hold control words (completion tickets of fused kernels) that
+ *     every call leaves zero again, so later calls need no clearing.
  *   - moe_forward and moe_graph_launch only enqueue work on `stream` (a
  *     hipStream_t; NULL means the null stream): no host synchronisation.
  *   - Calls that share one workspace must not overlap in time.
@@ -114,9 +117,9 @@ moe_status moe_workspace_size(moe_handle h, int32_t T, size_t *bytes);
  *   slot_table   int32 [E], device memory, read when the kernels run
  *   w            the slot-indexed weight pool
  *   out          bf16 [T][d_model]
- *   workspace    at least moe_workspace_size(T) bytes; holds the routing
- *                (see moe_routing_view) and the device error flags after the
- *                call. */
+ *   workspace    at least moe_workspace_size(T) bytes, zero-filled before its
+ *                first use; holds the routing (see moe_routing_view) and the
+ *                device error flags after the call. */
 moe_status moe_forward(moe_handle h, int32_t T, const uint16_t *hidden, const float *router_w,
                        const float *router_bias, const int32_t *slot_table, const moe_weights *w,
                        uint16_t *out, void *workspace, size_t workspace_bytes, moe_stream stream);
@@ -141,6 +144,21 @@ moe_status moe_graph_launch(moe_handle h, moe_stream stream);
  * `workspace` raised.  Each forward clears the bits when it starts. */
 moe_status moe_device_flags(moe_handle h, const void *workspace, int32_t T, moe_stream stream,
                             uint32_t *flags);
+
+/* Optional stage timing for measurement.  With max_forwards > 0 the handle
+ * creates HIP events for that many forwards (a setup step: call it outside
+ * any timed or captured region), and each eager moe_forward records an event
+ * on its stream before the first and after every stage: router, regroup,
+ * gate/up GEMM, down GEMM, combine.  0 releases the events.  Graph captures
+ * never record stage events. */
+moe_status moe_set_stage_timing(moe_handle h, int32_t max_forwards);
+
+/* Waits for the last recorded forward, writes the summed milliseconds of each
+ * of the MOE_NUM_STAGES stages over the recorded forwards to ms[] and their
+ * number to *forwards, then starts a new recording.  n_stages must be
+ * >= MOE_NUM_STAGES. */
+#define MOE_NUM_STAGES 5
+moe_status moe_stage_times(moe_handle h, float *ms, int32_t n_stages, int32_t *forwards);
 
 /* Static text for a status code. */
 const char *moe_status_string(moe_status s);

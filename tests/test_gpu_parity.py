@@ -196,3 +196,24 @@ def test_zero_tokens_is_a_noop():
     out = g.layer.forward(x, g.router_w, g.router_b, g.slot_table, g.dw)
     torch.cuda.synchronize()
     assert out.shape == (0, case.shape.d_model)
+
+
+def test_one_workspace_across_token_counts_keeps_control_words_zero():
+    """The fused kernels' completion tickets live at the start of the workspace;
+    every call must leave them zero, whatever T the previous call had."""
+    torch = require_gpu()
+    case0 = synth.make_case("fine_tiny")
+    g = gpu_layer(case0)
+    ws = g.layer.new_workspace(300)
+    for T in (16, 5, 64, 1, 300, 16, 65, 3):
+        case = synth.make_case("fine_tiny", T=T)
+        say(f"fine_tiny: shared workspace, T={T}")
+        x = g.hidden(case.hidden)
+        out = g.layer.forward(x, g.router_w, g.router_b, g.slot_table, g.dw, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:256].abs().sum().item()) == 0, f"control words not cleared after T={T}"
+        ref = _oracle(case)
+        from gpu_util import bf16_bits_to_f64
+        assert_out_close(bf16_bits_to_f64(out), ref["out"])
+        idx = g.layer.routing(ws, T)["topk_idx"].cpu().numpy()
+        np.testing.assert_array_equal(idx, ref["topk_idx"])
