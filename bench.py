@@ -37,17 +37,29 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
 DECODE_BOUND = {"mixtral_decode": "hbm", "phi35_skew": "hbm", "fine_decode": "hbm", "tiny": "hbm",
                 "fine_tiny": "hbm", "mixtral_prefill": "mfma", "fine_prefill": "mfma"}
-KERNEL_OF_STAGE = {"gate_up": "gateup_swiglu_kernel", "down": "down_kernel"}
-GEMM_SOURCE = os.path.join(ROOT, "expert_ffn_layer_router_amd", "csrc", "grouped_gemm.hip")
+CSRC = os.path.join(ROOT, "expert_ffn_layer_router_amd", "csrc")
+STREAM_MAX_TOKENS = 64   # the library's decode (weight-streaming) family runs up to this T
+
+
+def kernel_of_stage(stage, T):
+    """Name prefix of the kernel that runs a GEMM stage for T tokens."""
+    if T <= STREAM_MAX_TOKENS:
+        return {"gate_up": "stream_gemm_kernel<true", "down": "stream_gemm_kernel<false"}[stage]
+    return {"gate_up": "gateup_swiglu_kernel", "down": "down_kernel"}[stage]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_sha(path=GEMM_SOURCE) -> str:
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def source_sha() -> str:
+    """Hash of the kernel sources (counter summaries are valid for one version)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as fh:
+                h.update(name.encode() + fh.read())
+    return h.hexdigest()[:16]
 
 
 # --------------------------------------------------------------------------- work accounting
@@ -104,29 +116,41 @@ def cpu_baseline(case, budget_s=15.0):
 
 
 # --------------------------------------------------------------------------- PMC summaries
-def summarize_pmc(directory, out_path, calib_path=None):
-    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from rocprofv3
-    --pmc CSV output under `directory`."""
+def _pmc_rows(directory):
     import csv
     per = {}
     for path in glob.glob(os.path.join(directory, "**", "*counter_collection*.csv"), recursive=True):
         with open(path) as fh:
             for row in csv.DictReader(fh):
-                name = row.get("Kernel_Name", "")
-                ctr = row.get("Counter_Name", "")
                 try:
                     val = float(row.get("Counter_Value", "nan"))
                 except ValueError:
                     continue
+                key = (row.get("Kernel_Name", ""), row.get("Counter_Name", ""))
                 disp = row.get("Dispatch_Id", "")
-                per.setdefault(name, {}).setdefault(ctr, {}).setdefault(disp, 0.0)
-                per[name][ctr][disp] += val
-    summary = {}
-    for name, ctrs in per.items():
-        summary[name] = {c: statistics.mean(v.values()) for c, v in ctrs.items()}
-    res = {"source_sha": source_sha(), "kernels": summary}
-    if calib_path:
-        res["copy_calibration"] = calib_path
+                per.setdefault(key, {}).setdefault(disp, 0.0)
+                per[key][disp] += val
+    return per
+
+
+def summarize_pmc(dirs, out_path, copy_dirs=(), copy_bytes=1 << 30, workload=""):
+    """Mean FETCH_SIZE / WRITE_SIZE per dispatch (KiB) of every kernel in the
+    rocprofv3 --pmc output directories `dirs`, and the scale that makes the
+    same counters read `copy_bytes` for a plain device copy of that size."""
+    kernels = {}
+    for d in dirs:
+        for (name, ctr), disp in _pmc_rows(d).items():
+            kernels.setdefault(name, {})[ctr] = statistics.mean(disp.values())
+    scale = {}
+    for d in copy_dirs:
+        for (name, ctr), disp in _pmc_rows(d).items():
+            if "copybuffer" in name.lower():  # the runtime's device-to-device copy kernel
+                v = max(disp.values())
+                if v > 0:
+                    # a copy reads copy_bytes and writes copy_bytes
+                    scale[ctr] = copy_bytes / (v * 1024.0)
+    res = {"workload": workload, "source_sha": source_sha(), "copy_bytes": copy_bytes,
+           "scale": scale, "kernels": kernels}
     with open(out_path, "w") as fh:
         json.dump(res, fh, indent=1)
     return res
@@ -134,18 +158,18 @@ def summarize_pmc(directory, out_path, calib_path=None):
 
 def load_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from committed counter summaries, if they
-    were taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as fh:
-        data = json.load(fh)
-    if data.get("source_sha") != source_sha():
-        return None
-    scale = float(data.get("copy_scale", 1.0))
-    for name, ctr in data.get("kernels", {}).items():
-        if kernel in name and "FETCH_SIZE" in ctr and "WRITE_SIZE" in ctr:
-            return (ctr["FETCH_SIZE"] + ctr["WRITE_SIZE"]) * 1024.0 * scale
+    were taken on the current kernel sources; else None."""
+    sha = source_sha()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_pmc.json"))):
+        with open(path) as fh:
+            data = json.load(fh)
+        if data.get("source_sha") != sha:
+            continue
+        sc = data.get("scale", {})
+        for name, ctr in data.get("kernels", {}).items():
+            if kernel in name and "FETCH_SIZE" in ctr and "WRITE_SIZE" in ctr:
+                return (ctr["FETCH_SIZE"] * sc.get("FETCH_SIZE", 1.0) +
+                        ctr["WRITE_SIZE"] * sc.get("WRITE_SIZE", 1.0)) * 1024.0
     return None
 
 
@@ -173,12 +197,14 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--summarize-pmc", metavar="DIR", nargs="+", help="rocprofv3 --pmc output directories")
+    ap.add_argument("--copy-pmc", metavar="DIR", nargs="*", default=[], help="--pmc runs of --copy-calibration")
     ap.add_argument("--pmc-out", metavar="JSON")
     args = ap.parse_args(argv)
 
     if args.summarize_pmc:
-        res = summarize_pmc(args.summarize_pmc, args.pmc_out or "pmc_summary.json")
+        res = summarize_pmc(args.summarize_pmc, args.pmc_out or "pmc_summary.json", args.copy_pmc,
+                            workload=args.config)
         print(json.dumps(res))
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -298,11 +324,11 @@ def main(argv=None):
         achieved = work[dom]["flops"] / dur_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS}
-    roof["kernel"] = KERNEL_OF_STAGE[dom]
+    roof["kernel"] = kernel_of_stage(dom, T)
     roof["kernel_us"] = stage_us[dom]
     roof["algorithmic_bytes"] = work[dom]["bytes"]
     roof["algorithmic_flops"] = work[dom]["flops"]
-    roof["traffic"] = load_traffic(args.config, KERNEL_OF_STAGE[dom])
+    roof["traffic"] = load_traffic(args.config, kernel_of_stage(dom, T))
 
     layer_s = ms_per_step * 1e-3
     result = {
