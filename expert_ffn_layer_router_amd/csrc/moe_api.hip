@@ -12,6 +12,26 @@
 #include "moe.h"
 #include "plan.h"
 
+namespace moe {
+
+void launch_gateup(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w, char* ws,
+                   hipStream_t s) {
+  if (p.family == GemmFamily::kStream)
+    launch_gateup_stream(c, p, hidden, w, ws, s);
+  else
+    launch_gateup_prefill(c, p, hidden, w, ws, s);
+}
+
+void launch_down(const moe_config& c, const Plan& p, const moe_weights& w, uint16_t* out, char* ws,
+                 hipStream_t s) {
+  if (p.family == GemmFamily::kStream)
+    launch_down_stream(c, p, w, out, ws, s);
+  else
+    launch_down_prefill(c, p, w, ws, s);
+}
+
+}  // namespace moe
+
 #define MOE_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace {
@@ -65,8 +85,8 @@ void make_plan(const moe_config& c, int T, Plan* p) {
     p->family = GemmFamily::kStream;
     p->tile_rows = T <= 16 ? 16 : 32;
   } else {
-    p->family = GemmFamily::kGeneric;
-    p->tile_rows = kTileRows;
+    p->family = GemmFamily::kPrefill;
+    p->tile_rows = kPrefillTileRows;
   }
   p->fused_small = T <= kStreamMaxTokens;
   if (T <= kStreamMaxTokens) {
@@ -85,8 +105,7 @@ void make_plan(const moe_config& c, int T, Plan* p) {
     const int blocks = std::max(1, p->max_tiles * (c.d_model / (64 * p->down_ncw)));
     p->down_split = largest_divisor_at_most(c.d_ff / kGemmKStep, (kDownStreamBlocks + blocks - 1) / blocks);
   } else {
-    const int blocks = std::max(1, p->max_tiles * (c.d_model / kGemmColsPerBlock));
-    p->down_split = largest_divisor_at_most(c.d_ff / kGemmKStep, (1024 + blocks - 1) / blocks);
+    p->down_split = 1;
   }
 
   size_t off = 0;
@@ -108,6 +127,8 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   p->perm = take(4 * R);
   p->inv = take(4 * R);
   p->tiles = take(16 * (size_t)p->max_tiles);
+  p->xsum = take(4 * (size_t)T);
+  p->hsum_part = take(4 * R * (size_t)(c.d_ff / 128));
   p->num_tiles = take(4);
   p->h = take(2 * R * (size_t)c.d_ff);
   p->y = take(4 * (size_t)p->down_split * R * (size_t)c.d_model);

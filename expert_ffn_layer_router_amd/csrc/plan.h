@@ -12,9 +12,8 @@
 namespace moe {
 
 constexpr int kRouterTokTile = 16;     // tokens per router wave
-constexpr int kTileRows = 64;          // rows of an expert group per generic-family GEMM tile
-constexpr int kGemmColsPerBlock = 128; // output columns per generic-family GEMM block (4 waves x 32)
-constexpr int kGemmKStep = 128;        // k per GEMM load step
+constexpr int kPrefillTileRows = 128;  // prefill family: rows of an expert group per GEMM tile
+constexpr int kGemmKStep = 128;        // granularity of the decode down GEMM's k-split
 constexpr int kPermuteThreads = 1024;
 constexpr int kStreamMaxTokens = 64;   // up to this T the decode (weight-streaming) family runs
 
@@ -32,21 +31,22 @@ constexpr int kStreamMaxNCW = MOE_STREAM_NCW;       // decode family: widest blo
 constexpr int kStreamBuffers = MOE_STREAM_BUFFERS;  // decode family: LDS stage buffers (stages in flight + 1)
 constexpr int kDownStreamBlocks = MOE_DOWN_BLOCKS;  // k-split the decode down GEMM up to about this many blocks
 
-enum class GemmFamily { kStream, kGeneric };
+enum class GemmFamily { kStream, kPrefill };
 
 struct Plan {
   int T = 0, R = 0;
-  GemmFamily family = GemmFamily::kGeneric;
+  GemmFamily family = GemmFamily::kPrefill;
   int router_split = 0;       // 0: few-token router; else k-splits of the tiled router
   int gateup_ncw = 1, down_ncw = 1;  // decode family: blocks of 64 x ncw output columns
-  int tile_rows = kTileRows;  // rows of an expert group per GEMM row tile
+  int tile_rows = kPrefillTileRows;  // rows of an expert group per GEMM row tile
   int down_split = 1;         // k-split of the down projection
   int max_tiles = 0;          // upper bound on GEMM row tiles
   bool fused_small = false;   // few tokens: router + top-k + regroup in one kernel, combine fused into down
   // byte offsets into the workspace; [ctrl, ctrl + ctrl_bytes) are control
   // words that must be zero before first use and are left zero by every call
   size_t ctrl = 0, ctrl_bytes = 0, flags = 0, logits = 0, topk_idx = 0, topk_w = 0, counts = 0,
-         offsets = 0, perm = 0, inv = 0, tiles = 0, num_tiles = 0, h = 0, y = 0, total = 0;
+         offsets = 0, perm = 0, inv = 0, tiles = 0, num_tiles = 0, xsum = 0, hsum_part = 0, h = 0, y = 0,
+         total = 0;
 };
 
 // Fills `p` for T tokens.  Pure host arithmetic.
@@ -68,6 +68,10 @@ void launch_gateup_stream(const moe_config& c, const Plan& p, const uint16_t* hi
                           char* ws, hipStream_t s);
 void launch_down_stream(const moe_config& c, const Plan& p, const moe_weights& w, uint16_t* out, char* ws,
                         hipStream_t s);
+// prefill family (prefill_gemm.hip)
+void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w,
+                           char* ws, hipStream_t s);
+void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& w, char* ws, hipStream_t s);
 void launch_combine(const moe_config& c, const Plan& p, uint16_t* out, char* ws, hipStream_t s);
 
 }  // namespace moe

@@ -207,17 +207,31 @@ __global__ __launch_bounds__(256) void router_logits_tiled_kernel(const uint16_t
   }
 }
 
-// One wave per token (many-token path).  Also clears the device error flags
-// of this forward.
+// One wave per token (many-token path): top-k, and the token's row sum
+// sum_k x[t][k] (fp64, rounded to fp32) that the prefill gate/up GEMM's
+// zero-point term needs.  Also clears the device error flags of this forward.
 __global__ __launch_bounds__(256) void router_topk_kernel(const double* __restrict__ logits, int nsplit,
-                                                          const float* __restrict__ bias, int T, int E,
-                                                          int k, int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_w,
+                                                          const float* __restrict__ bias,
+                                                          const uint16_t* __restrict__ hidden, int d, int T,
+                                                          int E, int k, int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w, float* __restrict__ xsum,
                                                           uint32_t* __restrict__ flags) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_token<false>(logits, nsplit, bias, T, E, k, t, threadIdx.x & 63, topk_idx, topk_w);
+  const int lane = threadIdx.x & 63;
+  topk_token<false>(logits, nsplit, bias, T, E, k, t, lane, topk_idx, topk_w);
+  double sx = 0.0;
+  for (int kk = lane * 8; kk < d; kk += 512) {
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(hidden + (size_t)t * d + kk);
+    const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sx += (double)__uint_as_float(xs[i] << 16) + (double)__uint_as_float(xs[i] & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sx += __shfl_xor(sx, off, 64);
+  if (lane == 0) xsum[t] = (float)sx;
 }
 
 void launch_router(const moe_config& c, const Plan& p, const uint16_t* hidden, const float* router_w,
@@ -237,8 +251,9 @@ void launch_router(const moe_config& c, const Plan& p, const uint16_t* hidden, c
   dim3 grid((p.T + kRtTok - 1) / kRtTok, (c.num_experts + kRtExp - 1) / kRtExp, p.router_split);
   router_logits_tiled_kernel<<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, c.num_experts,
                                                   c.d_model / p.router_split);
-  router_topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(logits, p.router_split, router_bias, p.T, c.num_experts,
-                                                   c.top_k, topk_idx, topk_w, flags);
+  router_topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(logits, p.router_split, router_bias, hidden, c.d_model, p.T,
+                                                   c.num_experts, c.top_k, topk_idx, topk_w,
+                                                   reinterpret_cast<float*>(ws + p.xsum), flags);
 }
 
 }  // namespace moe
