@@ -34,7 +34,6 @@ constexpr int kBK = 64;                 // k per stage
 constexpr int kARow = kBK * 2;          // 128 bytes of an activation row per stage
 constexpr int kWRow = kBK / 2;          // 32 bytes of a weight row per stage
 constexpr int kABytes = kBM * kARow;    // 16 KB
-constexpr int kNBuf = 2;
 
 __device__ __forceinline__ void load_lds16(const void* g, char* lds_base) {
   __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds_base, 16, 0, 0);
@@ -77,9 +76,11 @@ struct PrefillArgs {
 // NJ: 32-column MFMA blocks per wave; a block holds 2 x NJ x 32 weight rows.
 // GATEUP (NJ = 4): h = silu(x Wg^T) * (x Wu^T) for 128 rows x 128 columns,
 // plus the rows' partial sums of h over those columns.  !GATEUP: y = h Wd^T
-// for 128 rows x 64 NJ columns.
-template <bool GATEUP, int NJ>
-__global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
+// for 128 rows x 64 NJ columns.  kNBuf LDS stage buffers (kNBuf - 1 stages in
+// flight); OCC blocks per compute unit (2 keeps the accumulators in VGPRs
+// and lets two blocks hide each other's barriers and LDS latency).
+template <bool GATEUP, int NJ, int kNBuf, int OCC>
+__global__ __launch_bounds__(256, OCC) void prefill_gemm_kernel(PrefillArgs a) {
   constexpr int kWRows = 64 * NJ;             // weight rows per block
   constexpr int kWBytes = kWRows * kWRow;
   constexpr int kStage = kABytes + kWBytes;
@@ -169,14 +170,21 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(PrefillArgs a) {
     wr[j] = GATEUP ? (j < 2 ? 64 * wn + 32 * j : kWRows / 2 + 64 * wn + 32 * (j - 2)) : 32 * NJ * wn + 32 * j;
 
   const int nst = K / kBK;
-  issue(0);
+#pragma unroll
+  for (int st = 0; st < kNBuf - 1; ++st)
+    if (st < nst) issue(st);
   for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst) {
-      issue(st + 1);
+    if (st + kNBuf - 1 < nst) issue(st + kNBuf - 1);
+    // wait until stage st has landed: the stages issued after it may stay in flight
+    const int later = min(kNBuf - 1, nst - 1 - st);
+    if (kNBuf > 3 && later >= 3)
+      wait_vmem<(kNBuf > 3 ? 3 : 0) * (4 + kWI)>();
+    else if (kNBuf > 2 && later >= 2)
+      wait_vmem<(kNBuf > 2 ? 2 : 0) * (4 + kWI)>();
+    else if (later >= 1)
       wait_vmem<4 + kWI>();
-    } else {
+    else
       wait_vmem<0>();
-    }
     lds_barrier();
     const char* buf = smem + (st % kNBuf) * kStage;
     u32x4 bq[NJ];
@@ -288,7 +296,7 @@ void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* h
   a.h = reinterpret_cast<uint16_t*>(ws + p.h);
   a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
   dim3 grid(c.d_ff / 128, p.max_tiles);
-  prefill_gemm_kernel<true, 4><<<grid, 256, 0, s>>>(a);
+  prefill_gemm_kernel<true, 4, 2, 2><<<grid, 256, 0, s>>>(a);
 }
 
 void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& w, char* ws, hipStream_t s) {
@@ -307,9 +315,9 @@ void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& 
   a.y = reinterpret_cast<float*>(ws + p.y);
   a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
   if (c.d_model % 256 == 0) {
-    prefill_gemm_kernel<false, 4><<<dim3(c.d_model / 256, p.max_tiles), 256, 0, s>>>(a);
+    prefill_gemm_kernel<false, 4, 4, 1><<<dim3(c.d_model / 256, p.max_tiles), 256, 0, s>>>(a);
   } else {
-    prefill_gemm_kernel<false, 2><<<dim3(c.d_model / 128, p.max_tiles), 256, 0, s>>>(a);
+    prefill_gemm_kernel<false, 2, 2, 2><<<dim3(c.d_model / 128, p.max_tiles), 256, 0, s>>>(a);
   }
 }
 
