@@ -192,7 +192,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="mixtral_decode")
-    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--mode", choices=["layers", "graph", "eager"], default="layers",
+                    help="layers: one HIP graph replays the rotated layers back to back (a model's decode-step "
+                         "graph); graph: one graph per layer step; eager: plain launches")
     ap.add_argument("--rotations", type=int, default=0, help="weight-pool copies (0: enough to defeat the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
@@ -259,15 +261,31 @@ def main(argv=None):
     layers = [MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T)
               for _ in range(rot)]
     stream = torch.cuda.Stream()
+    multi = None
     if args.mode == "graph":
         with torch.cuda.stream(stream):
             for L, p in zip(layers, pools):
                 L.capture(x, rw, rb, st, p, out, ws, stream)
         stream.synchronize()
+    elif args.mode == "layers":
+        # one graph = the `rot` layers back to back, each with its own weights
+        for i in range(rot):  # warm the handles outside capture
+            layers[i].forward(x, rw, rb, st, pools[i], out=out, workspace=ws, stream=stream)
+        stream.synchronize()
+        multi = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(multi, stream=stream):
+            for L, p in zip(layers, pools):
+                L.forward(x, rw, rb, st, p, out=out, workspace=ws, stream=stream)
+        stream.synchronize()
+        args.steps = -(-args.steps // rot) * rot
+        args.warmup = -(-args.warmup // rot) * rot
 
     def step(i):
         if args.mode == "graph":
             layers[i % rot].replay(stream)
+        elif args.mode == "layers":
+            if i % rot == 0:
+                multi.replay()
         else:
             layers[i % rot].forward(x, rw, rb, st, pools[i % rot], out=out, workspace=ws, stream=stream)
 
@@ -337,7 +355,9 @@ def main(argv=None):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.config, "T": T, "d_model": shape.d_model, "d_ff": shape.d_ff,
                    "num_experts": shape.num_experts, "top_k": shape.top_k, "num_slots": shape.num_slots,
-                   "weights": "int4 codes + fp16 scale/zero-point per output row", "mode": args.mode,
+                   "weights": "int4 codes + fp16 scale/zero-point per output row",
+                   "mode": {"layers": f"HIP graph of {rot} consecutive layers (own weights each), replayed",
+                            "graph": "one HIP graph per layer step", "eager": "eager launches"}[args.mode],
                    "weight_pool_copies": rot, "parallelism": "single GPU"},
         "roofline": roof,
         "layer": {"algorithmic_bytes": work["layer"]["bytes"], "algorithmic_flops": work["layer"]["flops"],

@@ -12,10 +12,15 @@
 
 namespace moe {
 
+constexpr int kFusedLogitsLds = 4096;  // logits (T x E) the fused router's last block stages in LDS
+
 // Top-k of one token, run by one wave: add the bias to the (split-summed)
 // logits, then k rounds of a wave-wide arg-max over the experts not yet
 // chosen (largest logit, ties to the lower id), then
 // w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+// kCoherent: read the logits with device-scope coherent loads (they were
+// written by other blocks of the same kernel); otherwise plain loads, summing
+// nsplit k-split partials.
 template <bool kCoherent>
 __device__ void topk_token(const double* __restrict__ logits, int nsplit, const float* __restrict__ bias, int T,
                            int E, int k, int t, int lane, int32_t* __restrict__ topk_idx,
@@ -140,9 +145,57 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
     const double v = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
     store_coherent(&logits[(size_t)(t0 + lane) * E + e], v);
   }
-  // the last block to finish reads every block's logits
+  // the last block to finish does the top-k of every token and the regroup
   if (!last_block_ticket(ticket, gridDim.x * gridDim.y, &is_last)) return;
   if (threadIdx.x == 0) *flags = 0u;
+  if (T * E <= kFusedLogitsLds && T <= 256) {
+    // slot table and logits into LDS (logits transposed: lg[e * T + t]) in one round of loads
+    __shared__ double lg[kFusedLogitsLds];
+    __shared__ int32_t sslot[256];
+    __shared__ double sbias[256];
+    __shared__ int32_t sid[256 * 8];
+    for (int e = threadIdx.x; e < E; e += 256) {
+      sslot[e] = ra.slot_table[e];
+      sbias[e] = bias ? (double)bias[e] : 0.0;
+    }
+    __syncthreads();  // sbias ready
+    // biased logits, transposed: lg[e * T + t]
+    for (int i = threadIdx.x; i < T * E; i += 256) lg[(i % E) * T + i / E] = load_coherent(&logits[i]) + sbias[i % E];
+    __syncthreads();
+    // rank of every (token, expert): the experts that beat it -- a larger
+    // logit, or an equal logit and a lower id.  Rank r < k is choice r.
+    for (int i = threadIdx.x; i < T * E; i += 256) {
+      const int t = i % T, e = i / T;
+      const double l = lg[i];
+      int r = 0;
+      for (int e2 = 0; e2 < E; ++e2) {
+        const double l2 = lg[e2 * T + t];
+        r += (l2 > l) || (l2 == l && e2 < e);
+      }
+      if (r < k) sid[t * k + r] = e;
+    }
+    __syncthreads();
+    if (threadIdx.x < T) {
+      const int t = threadIdx.x;
+      const double l0 = lg[sid[t * k] * T + t];
+      float ex[8], den = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        ex[j] = expf((float)(lg[sid[t * k + j] * T + t] - l0));
+        den += ex[j];
+      }
+      for (int j = 0; j < k; ++j) {
+        topk_idx[(size_t)t * k + j] = sid[t * k + j];
+        topk_w[(size_t)t * k + j] = ex[j] / den;
+      }
+    }
+    __syncthreads();
+    RegroupArgs la = ra;
+    la.topk_idx = sid;
+    la.slot_table = sslot;
+    regroup_block<256>(la);
+    if (threadIdx.x == 0) reset_ticket(ticket);
+    return;
+  }
   for (int t = wave; t < T; t += 4) topk_token<true>(logits, 1, bias, T, E, k, t, lane, topk_idx, topk_w);
   __syncthreads();
   regroup_block<256>(ra);
@@ -154,6 +207,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
 // 4 x 4 block of logits.  Output: logits[split][t][e], summed in split order
 // by router_topk_kernel.
 constexpr int kRtTok = 64, kRtExp = 64, kRtK = 32;
+
 __global__ __launch_bounds__(256) void router_logits_tiled_kernel(const uint16_t* __restrict__ hidden,
                                                                   const float* __restrict__ wr,
                                                                   double* __restrict__ logits, int T, int d,
