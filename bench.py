@@ -45,7 +45,7 @@ def kernel_of_stage(stage, T):
     """Name prefix of the kernel that runs a GEMM stage for T tokens."""
     if T <= STREAM_MAX_TOKENS:
         return {"gate_up": "stream_gemm_kernel<true", "down": "stream_gemm_kernel<false"}[stage]
-    return {"gate_up": "gateup_swiglu_kernel", "down": "down_kernel"}[stage]
+    return {"gate_up": "prefill_gemm_kernel<true", "down": "prefill_gemm_kernel<false"}[stage]
 
 
 def log(msg):

@@ -83,7 +83,9 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   const int E = c.num_experts;
   if (T <= kStreamMaxTokens) {
     p->family = GemmFamily::kStream;
-    p->tile_rows = T <= 16 ? 16 : 32;
+    // 16-row tiles: skewed groups get more tiles (their weights then come
+    // mostly from L2 / MALL) instead of staging mostly empty activation rows
+    p->tile_rows = 16;
   } else {
     p->family = GemmFamily::kPrefill;
     p->tile_rows = kPrefillTileRows;
@@ -101,7 +103,7 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   // split the down projection's k range until the grid has enough blocks
   if (p->family == GemmFamily::kStream) {
     p->gateup_ncw = (kStreamMaxNCW >= 2 && c.d_ff % 128 == 0) ? 2 : 1;
-    p->down_ncw = (kStreamMaxNCW >= 2 && c.d_model % 128 == 0) ? 2 : 1;
+    p->down_ncw = (kStreamMaxNCWDown >= 2 && c.d_model % 128 == 0) ? 2 : 1;
     const int blocks = std::max(1, p->max_tiles * (c.d_model / (64 * p->down_ncw)));
     p->down_split = largest_divisor_at_most(c.d_ff / kGemmKStep, (kDownStreamBlocks + blocks - 1) / blocks);
   } else {

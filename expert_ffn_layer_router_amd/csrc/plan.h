@@ -18,7 +18,7 @@ constexpr int kPermuteThreads = 1024;
 constexpr int kStreamMaxTokens = 64;   // up to this T the decode (weight-streaming) family runs
 
 #ifndef MOE_DOWN_BLOCKS
-#define MOE_DOWN_BLOCKS 2048
+#define MOE_DOWN_BLOCKS 1024
 #endif
 #ifndef MOE_STREAM_NCW
 #define MOE_STREAM_NCW 1
@@ -30,6 +30,10 @@ constexpr int kStreamCols = 64;                     // decode family: narrowest 
 constexpr int kStreamMaxNCW = MOE_STREAM_NCW;       // decode family: widest block, 64 x this many columns
 constexpr int kStreamBuffers = MOE_STREAM_BUFFERS;  // decode family: LDS stage buffers (stages in flight + 1)
 constexpr int kDownStreamBlocks = MOE_DOWN_BLOCKS;  // k-split the decode down GEMM up to about this many blocks
+#ifndef MOE_STREAM_NCW_DOWN
+#define MOE_STREAM_NCW_DOWN MOE_STREAM_NCW
+#endif
+constexpr int kStreamMaxNCWDown = MOE_STREAM_NCW_DOWN;  // decode-family down GEMM: widest block, 64 x this
 
 enum class GemmFamily { kStream, kPrefill };
 

@@ -331,10 +331,7 @@ void launch_stream(const moe_config& c, const Plan& p, const StreamArgs& args, h
   constexpr int NBUF = kStreamBuffers;
   const int ncols = GATEUP ? c.d_ff : c.d_model;
   dim3 grid(ncols / (64 * NCW), p.max_tiles, GATEUP ? 1 : p.down_split);
-  switch (p.tile_rows / 16) {
-    case 1: stream_gemm_kernel<GATEUP, 1, NCW, NBUF><<<grid, 256, 0, s>>>(args); break;
-    default: stream_gemm_kernel<GATEUP, 2, NCW, NBUF><<<grid, 256, 0, s>>>(args); break;
-  }
+  stream_gemm_kernel<GATEUP, 1, NCW, NBUF><<<grid, 256, 0, s>>>(args);  // 16-row tiles
 }
 }  // namespace
 
