@@ -85,7 +85,7 @@ void make_plan(const moe_config& c, int T, Plan* p) {
     p->family = GemmFamily::kStream;
     // 16-row tiles: skewed groups get more tiles (their weights then come
     // mostly from L2 / MALL) instead of staging mostly empty activation rows
-    p->tile_rows = 16;
+    p->tile_rows = kStreamTileRows;
   } else {
     p->family = GemmFamily::kPrefill;
     p->tile_rows = kPrefillTileRows;

@@ -23,12 +23,9 @@ constexpr int kStreamMaxTokens = 64;   // up to this T the decode (weight-stream
 #ifndef MOE_STREAM_NCW
 #define MOE_STREAM_NCW 1
 #endif
-#ifndef MOE_STREAM_BUFFERS
-#define MOE_STREAM_BUFFERS 2
-#endif
 constexpr int kStreamCols = 64;                     // decode family: narrowest block (64 output columns)
 constexpr int kStreamMaxNCW = MOE_STREAM_NCW;       // decode family: widest block, 64 x this many columns
-constexpr int kStreamBuffers = MOE_STREAM_BUFFERS;  // decode family: LDS stage buffers (stages in flight + 1)
+constexpr int kStreamTileRows = 16;                 // decode family: rows of an expert group per tile
 constexpr int kDownStreamBlocks = MOE_DOWN_BLOCKS;  // k-split the decode down GEMM up to about this many blocks
 #ifndef MOE_STREAM_NCW_DOWN
 #define MOE_STREAM_NCW_DOWN MOE_STREAM_NCW

@@ -5,14 +5,15 @@
 // active experts run as one group GEMM; section 3.1: per-expert int4 weights
 // with their own scale and zero-point, dequantised on the load path.
 //
-// A block owns one row tile of one expert (MB x 16 rows of its group) and
+// A block owns one row tile of one expert (up to 16 rows of its group) and
 // 64 x NCW output columns; each of its 4 waves computes 16 x NCW of them.  The
 // k range is walked in stages of kStageK: per stage the block copies 128 bytes
 // of every weight row it needs (gate and up rows, or down rows) and 512 bytes
 // of every activation row straight from HBM into LDS (global_load_lds_dwordx4,
-// full 128-byte lines, several rows per instruction) into a ring of NBUF
-// buffers, so NBUF - 1 stages are in flight while one is multiplied.  Wider
-// blocks (NCW = 2) halve the activation bytes staged per weight byte.  The 16-byte
+// full 128-byte lines, several rows per instruction) into one of two
+// buffers, so the next stage is in flight while one is multiplied; activation
+// rows past the tile's end are not copied.  Wider blocks (NCW = 2) halve the
+// activation bytes staged per weight byte.  The 16-byte
 // chunks are XOR-swizzled in LDS so that the MFMA fragment reads are free of
 // bank conflicts.  Codes are widened to bf16 in registers (codes_to_bf16) and
 // the scale / zero-point are applied in the epilogue; the row sums of A the
@@ -59,20 +60,36 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// LDS reads written as inline assembly.  The compiler treats a plain LDS read
+// as depending on every direct-to-LDS copy still in flight (it cannot tell
+// the two stage buffers apart) and waits for all of them, next stage included,
+// which would serialise the copy pipeline.  These reads are ordered by the
+// explicit waits and barriers instead: lds_wait() waits for the wave's LDS
+// reads, and lds_ready(v) makes each value depend on that wait, so no use of
+// v is scheduled before it.
+__device__ __forceinline__ u32x4 lds_read16(const char* p) {
+  u32x4 v;
+  const uint32_t addr = (uint32_t)(uintptr_t)(const lds_void*)p;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_ready(u32x4& v) { asm volatile("" : "+v"(v)); }
+
 // Swizzled 16-byte chunk positions inside a stage buffer.
 __device__ __forceinline__ int wchunk_pos(int row, int c) { return c ^ ((row >> 1) & 7); }  // c < 8
 __device__ __forceinline__ int achunk_pos(int row, int q) { return q ^ (row & 15); }         // q < 32
 
-// wait until stage st has landed when `later` full stages were issued after it
-template <int PER_STAGE, int NBUF>
-__device__ __forceinline__ void wait_stage(int later) {
-  if (NBUF > 2 && later >= 2) {
-    wait_vmem<(NBUF > 2 ? 2 : 0) * PER_STAGE>();
-  } else if (later >= 1) {
-    wait_vmem<PER_STAGE>();
-  } else {
-    wait_vmem<0>();
+// wait_vmem with a run-time count n in [BASE, BASE + EXTRA]
+template <int BASE, int EXTRA>
+__device__ __forceinline__ void wait_vmem_rt(int n) {
+  if constexpr (EXTRA > 0) {
+    if (n > BASE) {
+      wait_vmem_rt<BASE + 1, EXTRA - 1>(n);
+      return;
+    }
   }
+  wait_vmem<BASE>();
 }
 
 }  // namespace
@@ -105,16 +122,16 @@ struct StreamArgs {
 // !GATEUP: ypart[split][p] = h[p] Wd^T over the k range of `split`, fp32,
 // written with coherent stores; with a FusedCombine, the last block of each
 // column slice also writes that slice of out[].
-template <bool GATEUP, int MB, int NCW, int NBUF>
+template <bool GATEUP, int NCW>
 __global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
   constexpr int COLS = 64 * NCW;                        // output columns per block
   constexpr int NWR = (GATEUP ? 2 : 1) * COLS;          // weight rows per stage
-  constexpr int WBYTES = NWR * kWRowBytes, ABYTES = MB * 16 * kARowBytes;
+  constexpr int WBYTES = NWR * kWRowBytes, ABYTES = kStreamTileRows * kARowBytes;
   constexpr int SBYTES = WBYTES + ABYTES;
   constexpr int WI = NWR / kRowsPerWInst / 4;           // weight-load instructions per wave per stage
-  constexpr int AI = MB * 16 / kRowsPerAInst / 4;       // activation-load instructions per wave per stage
-  static_assert(WI * kRowsPerWInst * 4 == NWR && AI * kRowsPerAInst * 4 == MB * 16, "even split over waves");
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * SBYTES];
+  constexpr int AI = kStreamTileRows / kRowsPerAInst / 4;  // activation-load instructions per wave per stage
+  static_assert(WI * kRowsPerWInst * 4 == NWR && AI * kRowsPerAInst * 4 == kStreamTileRows, "even split over waves");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * SBYTES];
   __shared__ int is_last;
 
   const int ntiles = *a.num_tiles;
@@ -123,9 +140,8 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, grp = lane >> 4;
   const int n0 = blockIdx.x * COLS;
-  const int4 td = a.tiles[tile];  // (expert, slot, first grouped row, rows)
+  const int4 td = a.tiles[tile];  // (expert, slot, first grouped row, rows <= 16)
   const int slot = td.y, pbase = td.z, rows = td.w;
-  const int nmb = (rows + 15) >> 4;
   const int ncols_total = GATEUP ? a.dff : a.d;   // output columns of this GEMM
   const int K = GATEUP ? a.d : a.kchunk;          // k range of this block
   const int kbeg = GATEUP ? 0 : blockIdx.z * a.kchunk;
@@ -139,10 +155,9 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
 #pragma unroll
     for (int cb = 0; cb < NCW; ++cb) {
       const int n = n0 + wave * 16 * NCW + cb * 16 + lr;
-      for (int row = grp * 4; row < rows; row += 16)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (row + i < rows) store_coherent(&yrow[(size_t)(row + i) * a.d + n], 0.0f);
+      for (int i = 0; i < 4; ++i)
+        if (grp * 4 + i < rows) store_coherent(&yrow[(size_t)(grp * 4 + i) * a.d + n], 0.0f);
     }
   } else {
     // activation row sources (gate/up: tokens through perm -- dependent loads first)
@@ -164,7 +179,7 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
     const int nst = (K + kStageK - 1) / kStageK;
     const bool half_last = (K % kStageK) != 0;
     auto issue_w = [&](int st) {
-      char* buf = smem + (st % NBUF) * SBYTES;
+      char* buf = smem + (st & 1) * SBYTES;
       const bool half = half_last && st == nst - 1;
 #pragma unroll
       for (int j = 0; j < WI; ++j) {
@@ -182,87 +197,77 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
                                     : a.act + (size_t)arow[j] * a.dff + kbeg;
       asrc[j] = reinterpret_cast<const uint8_t*>(rowp) + 16 * achunk_pos(m, lane % 32);
     }
+    // Activation rows past the tile's end are not copied (their LDS rows hold
+    // stale data, which only reaches output rows that are never stored).  An
+    // instruction whose rows all lie past the end is not issued at all: na of
+    // this wave's AI instructions are, the same number every stage.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int na = min(AI, max(0, (rows - wave_u * AI * kRowsPerAInst + kRowsPerAInst - 1) / kRowsPerAInst));
     auto issue_a = [&](int st) {
-      char* buf = smem + (st % NBUF) * SBYTES;
+      char* buf = smem + (st & 1) * SBYTES;
       const bool half = half_last && st == nst - 1;
 #pragma unroll
       for (int j = 0; j < AI; ++j) {
-        const int m = (wave * AI + j) * kRowsPerAInst + lane / 32;
-        if (!half || achunk_pos(m, lane % 32) < 16)
-          load_lds16(asrc[j] + (size_t)st * kARowBytes, buf + WBYTES + (wave * AI + j) * 1024);
+        if (j < na) {
+          const int m = (wave * AI + j) * kRowsPerAInst + lane / 32;
+          if (m < rows && (!half || achunk_pos(m, lane % 32) < 16))
+            load_lds16(asrc[j] + (size_t)st * kARowBytes, buf + WBYTES + (wave * AI + j) * 1024);
+        }
       }
     };
     issue_a(0);
-#pragma unroll
-    for (int st = 1; st < NBUF - 1; ++st) {
-      if (st < nst) {
-        issue_w(st);
-        issue_a(st);
-      }
-    }
 
-    f32x4 acc0[MB][NCW], acc1[MB][NCW], accs[MB];
+    f32x4 acc0[NCW], acc1[NCW], accs = {0, 0, 0, 0};
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      accs[mb] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int cb = 0; cb < NCW; ++cb) acc0[mb][cb] = acc1[mb][cb] = f32x4{0, 0, 0, 0};
-    }
+    for (int cb = 0; cb < NCW; ++cb) acc0[cb] = acc1[cb] = f32x4{0, 0, 0, 0};
     const u32x4 ones = ones_bf16();
 
     for (int st = 0; st < nst; ++st) {
-      const int ahead = st + NBUF - 1;
-      if (ahead < nst) {
-        issue_w(ahead);
-        issue_a(ahead);
+      if (st + 1 < nst) {
+        issue_w(st + 1);
+        issue_a(st + 1);
       }
-      // full stages issued after st (a half stage counts as none: wait longer, never shorter)
-      int later = min(NBUF - 1, nst - 1 - st);
-      if (half_last && later > 0 && st + later == nst - 1) --later;
-      wait_stage<WI + AI, NBUF>(later);
+      // wait for this stage's copies; the next stage's (WI + na instructions,
+      // unless it is a half stage, which counts as none: wait longer, never
+      // shorter) stay in flight
+      if (st + 1 < nst && !(half_last && st + 1 == nst - 1))
+        wait_vmem_rt<WI, AI>(WI + na);
+      else
+        wait_vmem<0>();
       lds_barrier();
-      const char* buf = smem + (st % NBUF) * SBYTES;
+      const char* buf = smem + (st & 1) * SBYTES;
       const int nss = (half_last && st == nst - 1) ? 1 : 2;
       for (int ss = 0; ss < nss; ++ss) {
         const int c = 4 * ss + grp;
-        u32x4 b0[NCW], b1[NCW];
+        u32x4 b0[NCW], b1[NCW], av[4];
 #pragma unroll
         for (int cb = 0; cb < NCW; ++cb) {
           const int r0 = wave * 16 * NCW + cb * 16 + lr;
-          b0[cb] = *reinterpret_cast<const u32x4*>(buf + r0 * kWRowBytes + 16 * wchunk_pos(r0, c));
+          b0[cb] = lds_read16(buf + r0 * kWRowBytes + 16 * wchunk_pos(r0, c));
           if (GATEUP) {
             const int r1 = COLS + r0;
-            b1[cb] = *reinterpret_cast<const u32x4*>(buf + r1 * kWRowBytes + 16 * wchunk_pos(r1, c));
+            b1[cb] = lds_read16(buf + r1 * kWRowBytes + 16 * wchunk_pos(r1, c));
           }
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int q = 16 * ss + 4 * grp + s;
-          u32x4 av[MB];
+        for (int s = 0; s < 4; ++s) av[s] = lds_read16(buf + WBYTES + lr * kARowBytes + 16 * achunk_pos(lr, 16 * ss + 4 * grp + s));
+        lds_wait();
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            if (mb < nmb) {
-              const int m = mb * 16 + lr;
-              const u32x4 raw = *reinterpret_cast<const u32x4*>(buf + WBYTES + m * kARowBytes + 16 * achunk_pos(m, q));
-              av[mb] = GATEUP ? permute_a(raw) : raw;  // h is stored in fragment order already
-            }
-          }
+        for (int cb = 0; cb < NCW; ++cb) {
+          lds_ready(b0[cb]);
+          if (GATEUP) lds_ready(b1[cb]);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) lds_ready(av[s]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 x = GATEUP ? permute_a(av[s]) : av[s];  // h is stored in fragment order already
 #pragma unroll
           for (int cb = 0; cb < NCW; ++cb) {
-            const u32x4 bb0 = codes_to_bf16(b0[cb][s]);
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              if (mb < nmb) acc0[mb][cb] = mfma16(av[mb], bb0, acc0[mb][cb]);
-            if (GATEUP) {
-              const u32x4 bb1 = codes_to_bf16(b1[cb][s]);
-#pragma unroll
-              for (int mb = 0; mb < MB; ++mb)
-                if (mb < nmb) acc1[mb][cb] = mfma16(av[mb], bb1, acc1[mb][cb]);
-            }
+            acc0[cb] = mfma16(x, codes_to_bf16(b0[cb][s]), acc0[cb]);
+            if (GATEUP) acc1[cb] = mfma16(x, codes_to_bf16(b1[cb][s]), acc1[cb]);
           }
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            if (mb < nmb) accs[mb] = mfma16(av[mb], ones, accs[mb]);
+          accs = mfma16(x, ones, accs);
         }
       }
       lds_barrier();
@@ -279,21 +284,16 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
         cc1 = kCodeBias + fp16_to_f32(a.z1[sidx]);
       }
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        if (mb < nmb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = mb * 16 + grp * 4 + i;
-            if (row < rows) {
-              const float sx = accs[mb][i];
-              const float v0 = sc0 * (acc0[mb][cb][i] - cc0 * sx);
-              if (GATEUP) {
-                const float v1 = sc1 * (acc1[mb][cb][i] - cc1 * sx);
-                a.h[(size_t)(pbase + row) * a.dff + h_phys_col(n)] = f32_to_bf16(silu(v0) * v1);
-              } else {
-                store_coherent(&yrow[(size_t)row * a.d + n], v0);
-              }
-            }
+      for (int i = 0; i < 4; ++i) {
+        const int row = grp * 4 + i;
+        if (row < rows) {
+          const float sx = accs[i];
+          const float v0 = sc0 * (acc0[cb][i] - cc0 * sx);
+          if (GATEUP) {
+            const float v1 = sc1 * (acc1[cb][i] - cc1 * sx);
+            a.h[(size_t)(pbase + row) * a.dff + h_phys_col(n)] = f32_to_bf16(silu(v0) * v1);
+          } else {
+            store_coherent(&yrow[(size_t)row * a.d + n], v0);
           }
         }
       }
@@ -328,10 +328,9 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
 namespace {
 template <bool GATEUP, int NCW>
 void launch_stream(const moe_config& c, const Plan& p, const StreamArgs& args, hipStream_t s) {
-  constexpr int NBUF = kStreamBuffers;
   const int ncols = GATEUP ? c.d_ff : c.d_model;
   dim3 grid(ncols / (64 * NCW), p.max_tiles, GATEUP ? 1 : p.down_split);
-  stream_gemm_kernel<GATEUP, 1, NCW, NBUF><<<grid, 256, 0, s>>>(args);  // 16-row tiles
+  stream_gemm_kernel<GATEUP, NCW><<<grid, 256, 0, s>>>(args);
 }
 }  // namespace
 
