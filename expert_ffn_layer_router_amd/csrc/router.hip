@@ -149,8 +149,9 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
   if (!last_block_ticket(ticket, gridDim.x * gridDim.y, &is_last)) return;
   if (threadIdx.x == 0) *flags = 0u;
   if (T * E <= kFusedLogitsLds && T <= 256) {
-    // slot table and logits into LDS (logits transposed: lg[e * T + t]) in one round of loads
-    __shared__ double lg[kFusedLogitsLds];
+    // slot table and the biased logits, rounded to fp32, into LDS (transposed:
+    // lgf[e * T + t]) in one round of loads; the fp64 values stay in global memory
+    __shared__ float lgf[kFusedLogitsLds];
     __shared__ int32_t sslot[256];
     __shared__ double sbias[256];
     __shared__ int32_t sid[256 * 8];
@@ -159,28 +160,54 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
       sbias[e] = bias ? (double)bias[e] : 0.0;
     }
     __syncthreads();  // sbias ready
-    // biased logits, transposed: lg[e * T + t]
-    for (int i = threadIdx.x; i < T * E; i += 256) lg[(i % E) * T + i / E] = load_coherent(&logits[i]) + sbias[i % E];
+    for (int i = threadIdx.x; i < T * E; i += 256) lgf[(i % E) * T + i / E] = (float)(load_coherent(&logits[i]) + sbias[i % E]);
     __syncthreads();
     // rank of every (token, expert): the experts that beat it -- a larger
-    // logit, or an equal logit and a lower id.  Rank r < k is choice r.
+    // logit, or an equal logit and a lower id.  Rank r < k is choice r.  The
+    // counting runs on the fp32 copies, without branches and with 8 LDS reads
+    // in flight: rounding is monotonic, so a strictly larger (smaller) fp32
+    // value means a strictly larger (smaller) fp64 one; a pair whose fp32
+    // values tie is counted again exactly in fp64.
     for (int i = threadIdx.x; i < T * E; i += 256) {
       const int t = i % T, e = i / T;
-      const double l = lg[i];
-      int r = 0;
-      for (int e2 = 0; e2 < E; ++e2) {
-        const double l2 = lg[e2 * T + t];
-        r += (l2 > l) || (l2 == l && e2 < e);
+      const float f = lgf[i];
+      int r = 0, tie = 0, e2 = 0;
+      for (; e2 + 8 <= E; e2 += 8) {
+        float f2[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) f2[u] = lgf[(e2 + u) * T + t];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          r += (int)(f2[u] > f);
+          tie |= (int)(f2[u] == f) & (int)(e2 + u != e);
+        }
+      }
+      for (; e2 < E; ++e2) {
+        const float f2 = lgf[e2 * T + t];
+        r += (int)(f2 > f);
+        tie |= (int)(f2 == f) & (int)(e2 != e);
+      }
+      if (tie) {  // rare: count again in fp64
+        const double l = load_coherent(&logits[(size_t)t * E + e]) + sbias[e];
+        r = 0;
+        for (int e3 = 0; e3 < E; ++e3) {
+          const double l2 = load_coherent(&logits[(size_t)t * E + e3]) + sbias[e3];
+          r += (int)(l2 > l) | ((int)(l2 == l) & (int)(e3 < e));
+        }
       }
       if (r < k) sid[t * k + r] = e;
     }
     __syncthreads();
     if (threadIdx.x < T) {
       const int t = threadIdx.x;
-      const double l0 = lg[sid[t * k] * T + t];
+      double lc[8];  // the chosen biased logits, fp64
+      for (int j = 0; j < k; ++j) {
+        const int e = sid[t * k + j];
+        lc[j] = load_coherent(&logits[(size_t)t * E + e]) + sbias[e];
+      }
       float ex[8], den = 0.0f;
       for (int j = 0; j < k; ++j) {
-        ex[j] = expf((float)(lg[sid[t * k + j] * T + t] - l0));
+        ex[j] = expf((float)(lc[j] - lc[0]));
         den += ex[j];
       }
       for (int j = 0; j < k; ++j) {
