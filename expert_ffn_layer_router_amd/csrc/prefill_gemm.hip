@@ -86,9 +86,13 @@ __global__ __launch_bounds__(256, OCC) void prefill_gemm_kernel(PrefillArgs a) {
   constexpr int kStage = kABytes + kWBytes;
   constexpr int kWI = NJ / 2;                 // weight-load instructions per wave per stage
   static_assert(!GATEUP || NJ == 4, "gate/up blocks pair 2 gate and 2 up column blocks per wave");
-  __shared__ __attribute__((aligned(1024))) char smem[kNBuf * kStage];
-  __shared__ float rowsum[kBM];
-  __shared__ float hpart[2][kBM];
+  // One LDS object for the stage ring and the row sums: with several, the
+  // compiler's alias information makes every LDS read wait for all
+  // direct-to-LDS copies in flight (next stages included); the explicit
+  // vmcnt waits below order the reads instead.
+  __shared__ __attribute__((aligned(1024))) char smem[kNBuf * kStage + 3 * kBM * 4];
+  float* rowsum = reinterpret_cast<float*>(smem + kNBuf * kStage);       // [kBM]
+  float (*hpart)[kBM] = reinterpret_cast<float (*)[kBM]>(rowsum + kBM);  // [2][kBM]
   const int ntiles = *a.num_tiles;
   const int tile = blockIdx.y;
   if (tile >= ntiles) return;
