@@ -57,12 +57,20 @@ __device__ __forceinline__ int h_phys_col(int n) {
 //     sum_k a_k (q_k - z) s = s * (acc - (128 + z) * sum_k a_k).
 constexpr float kCodeBias = 128.0f;
 
+// Each output is one v_and_or_b32.  That encoding takes no literal constants,
+// so with literal masks the compiler splits it into an and and an or; the two
+// constants are therefore materialised opaquely (an SGPR and a VGPR, hoisted
+// out of loops) and the and-or itself stays compiler-generated, so that the
+// compiler still sees the writes the matrix cores read.
 __device__ __forceinline__ u32x4 codes_to_bf16(uint32_t w) {
+  uint32_t mask, bias;
+  asm("s_mov_b32 %0, 0x000f000f" : "=s"(mask));
+  asm("v_mov_b32 %0, 0x43004300" : "=v"(bias));
   u32x4 r;
-  r.x = (w & 0x000F000Fu) | 0x43004300u;          // (q0, q4)
-  r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;   // (q1, q5)
-  r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;   // (q2, q6)
-  r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;  // (q3, q7)
+  r.x = (w & mask) | bias;          // (q0, q4)
+  r.y = ((w >> 4) & mask) | bias;   // (q1, q5)
+  r.z = ((w >> 8) & mask) | bias;   // (q2, q6)
+  r.w = ((w >> 12) & mask) | bias;  // (q3, q7)
   return r;
 }
 

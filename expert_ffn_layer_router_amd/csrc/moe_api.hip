@@ -134,6 +134,8 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   p->num_tiles = take(4);
   p->h = take(2 * R * (size_t)c.d_ff);
   p->y = take(4 * (size_t)p->down_split * R * (size_t)c.d_model);
+  // prefill: x in the GEMMs' fragment k-order
+  p->xperm = take(p->family == GemmFamily::kPrefill ? 2 * (size_t)T * c.d_model : 0);
   p->total = off;
 }
 

@@ -13,7 +13,9 @@
 // walked in stages of 64: per stage the activation tile (128 rows x 128 B)
 // and the int4 weight tile (256 rows x 32 B) are copied from global memory
 // straight into LDS (global_load_lds_dwordx4), double-buffered and
-// XOR-swizzled for conflict-free fragment reads.  Each lane widens one 32-bit
+// XOR-swizzled for conflict-free fragment reads.  Both A operands (x, copied
+// by the router's top-k kernel, and h) are stored in the fragment k-order of
+// the codes, so fragments go to the matrix cores as read.  Each lane widens one 32-bit
 // word of codes into a bf16 B fragment (codes_to_bf16); scale and zero-point
 // are applied in the epilogue with precomputed row sums of A (token row sums
 // from the router, h row sums from the gate/up epilogue), which keeps the
@@ -34,6 +36,21 @@ constexpr int kBK = 64;                 // k per stage
 constexpr int kARow = kBK * 2;          // 128 bytes of an activation row per stage
 constexpr int kWRow = kBK / 2;          // 32 bytes of a weight row per stage
 constexpr int kABytes = kBM * kARow;    // 16 KB
+#ifndef MOE_PF_GU_STAGES
+#define MOE_PF_GU_STAGES 2
+#endif
+#ifndef MOE_PF_GU_BLOCKS
+#define MOE_PF_GU_BLOCKS 2
+#endif
+#ifndef MOE_PF_DN_STAGES
+#define MOE_PF_DN_STAGES 2
+#endif
+#ifndef MOE_PF_DN_BLOCKS
+#define MOE_PF_DN_BLOCKS 2
+#endif
+// stage buffers (copies in flight + 1) and blocks per compute unit aimed for
+constexpr int kPrefillGateUpStages = MOE_PF_GU_STAGES, kPrefillGateUpBlocks = MOE_PF_GU_BLOCKS;
+constexpr int kPrefillDownStages = MOE_PF_DN_STAGES, kPrefillDownBlocks = MOE_PF_DN_BLOCKS;
 
 __device__ __forceinline__ void load_lds16(const void* g, char* lds_base) {
   __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds_base, 16, 0, 0);
@@ -204,7 +221,7 @@ __global__ __launch_bounds__(256, OCC) void prefill_gemm_kernel(PrefillArgs a) {
       for (int i = 0; i < 2; ++i) {
         const int r = 64 * wm + 32 * i + l32;
         const u32x4 raw = *reinterpret_cast<const u32x4*>(buf + r * kARow + 16 * apos(r, 4 * hh + s));
-        av[i] = GATEUP ? permute_a(raw) : raw;  // h is stored in fragment order already
+        av[i] = raw;  // x and h are stored in fragment order already
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -281,7 +298,8 @@ __global__ __launch_bounds__(256, OCC) void prefill_gemm_kernel(PrefillArgs a) {
 void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w,
                            char* ws, hipStream_t s) {
   PrefillArgs a{};
-  a.act = hidden;
+  (void)hidden;  // read through the router's copy of x in fragment k-order
+  a.act = reinterpret_cast<const uint16_t*>(ws + p.xperm);
   a.perm = reinterpret_cast<const int32_t*>(ws + p.perm);
   a.tiles = reinterpret_cast<const int4*>(ws + p.tiles);
   a.num_tiles = reinterpret_cast<const int32_t*>(ws + p.num_tiles);
@@ -300,7 +318,7 @@ void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* h
   a.h = reinterpret_cast<uint16_t*>(ws + p.h);
   a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
   dim3 grid(c.d_ff / 128, p.max_tiles);
-  prefill_gemm_kernel<true, 4, 2, 2><<<grid, 256, 0, s>>>(a);
+  prefill_gemm_kernel<true, 4, kPrefillGateUpStages, kPrefillGateUpBlocks><<<grid, 256, 0, s>>>(a);
 }
 
 void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& w, char* ws, hipStream_t s) {
@@ -319,7 +337,7 @@ void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& 
   a.y = reinterpret_cast<float*>(ws + p.y);
   a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
   if (c.d_model % 256 == 0) {
-    prefill_gemm_kernel<false, 4, 4, 1><<<dim3(c.d_model / 256, p.max_tiles), 256, 0, s>>>(a);
+    prefill_gemm_kernel<false, 4, kPrefillDownStages, kPrefillDownBlocks><<<dim3(c.d_model / 256, p.max_tiles), 256, 0, s>>>(a);
   } else {
     prefill_gemm_kernel<false, 2, 2, 2><<<dim3(c.d_model / 128, p.max_tiles), 256, 0, s>>>(a);
   }

@@ -296,15 +296,18 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const double* __restri
                                                           const uint16_t* __restrict__ hidden, int d, int T,
                                                           int E, int k, int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ topk_w, float* __restrict__ xsum,
-                                                          uint32_t* __restrict__ flags) {
+                                                          uint16_t* __restrict__ xperm, uint32_t* __restrict__ flags) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
   topk_token<false>(logits, nsplit, bias, T, E, k, t, lane, topk_idx, topk_w);
+  // row sum of x (for the gate/up GEMM's zero-point term) and x in fragment
+  // k-order (the gate/up GEMM's A operand then needs no permutes)
   double sx = 0.0;
   for (int kk = lane * 8; kk < d; kk += 512) {
     const u32x4 xv = *reinterpret_cast<const u32x4*>(hidden + (size_t)t * d + kk);
+    *reinterpret_cast<u32x4*>(xperm + (size_t)t * d + kk) = permute_a(xv);
     const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -334,7 +337,8 @@ void launch_router(const moe_config& c, const Plan& p, const uint16_t* hidden, c
                                                   c.d_model / p.router_split);
   router_topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(logits, p.router_split, router_bias, hidden, c.d_model, p.T,
                                                    c.num_experts, c.top_k, topk_idx, topk_w,
-                                                   reinterpret_cast<float*>(ws + p.xsum), flags);
+                                                   reinterpret_cast<float*>(ws + p.xsum),
+                                                   reinterpret_cast<uint16_t*>(ws + p.xperm), flags);
 }
 
 }  // namespace moe
