@@ -89,7 +89,12 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (about 1 ulp
+// each, far below the bf16 rounding h gets next).  Saturates correctly:
+// e^-g -> inf gives g * 0, e^-g -> 0 gives g.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+}
 
 // Hand-over between blocks of one kernel without flushing caches.  The L2 of
 // each XCD is not coherent with the others for ordinary accesses, and a

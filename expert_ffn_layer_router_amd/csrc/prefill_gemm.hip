@@ -40,7 +40,7 @@ constexpr int kABytes = kBM * kARow;    // 16 KB
 #define MOE_PF_GU_STAGES 2
 #endif
 #ifndef MOE_PF_GU_BLOCKS
-#define MOE_PF_GU_BLOCKS 2
+#define MOE_PF_GU_BLOCKS 1
 #endif
 #ifndef MOE_PF_DN_STAGES
 #define MOE_PF_DN_STAGES 2
@@ -51,6 +51,19 @@ constexpr int kABytes = kBM * kARow;    // 16 KB
 // stage buffers (copies in flight + 1) and blocks per compute unit aimed for
 constexpr int kPrefillGateUpStages = MOE_PF_GU_STAGES, kPrefillGateUpBlocks = MOE_PF_GU_BLOCKS;
 constexpr int kPrefillDownStages = MOE_PF_DN_STAGES, kPrefillDownBlocks = MOE_PF_DN_BLOCKS;
+#ifndef MOE_PF_GU_NJ
+#define MOE_PF_GU_NJ 8
+#endif
+#ifndef MOE_PF_GU_NW
+#define MOE_PF_GU_NW 8
+#endif
+#ifndef MOE_PF_DN_NW
+#define MOE_PF_DN_NW 4
+#endif
+// gate/up blocks: 64 NJ weight rows (32 NJ output columns) on NW waves, 1 x NW;
+// down blocks: 256 weight rows on NW waves, 1 x NW
+constexpr int kPrefillGateUpNJ = MOE_PF_GU_NJ, kPrefillGateUpWaves = MOE_PF_GU_NW;
+constexpr int kPrefillDownWaves = MOE_PF_DN_NW;
 
 __device__ __forceinline__ void load_lds16(const void* g, char* lds_base) {
   __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds_base, 16, 0, 0);
@@ -80,7 +93,8 @@ struct PrefillArgs {
   const int4* tiles;
   const int32_t* num_tiles;
   const float* xsum;          // gate/up: [T] row sums of hidden
-  float* hsum_part;           // gate/up writes, down reads: [R][dff / 128]
+  float* hsum_part;           // gate/up writes, down reads: [R][hparts]
+  int hparts;                 // gate/up column blocks (partial h row sums per row)
   int num_slots, d, dff, topk;
   const uint8_t* w0;          // gate (or down) codes
   const uint8_t* w1;          // up codes
@@ -90,31 +104,40 @@ struct PrefillArgs {
   uint32_t* flags;
 };
 
-// NJ: 32-column MFMA blocks per wave; a block holds 2 x NJ x 32 weight rows.
-// GATEUP (NJ = 4): h = silu(x Wg^T) * (x Wu^T) for 128 rows x 128 columns,
-// plus the rows' partial sums of h over those columns.  !GATEUP: y = h Wd^T
-// for 128 rows x 64 NJ columns.  kNBuf LDS stage buffers (kNBuf - 1 stages in
-// flight); OCC blocks per compute unit (2 keeps the accumulators in VGPRs
-// and lets two blocks hide each other's barriers and LDS latency).
-template <bool GATEUP, int NJ, int kNBuf, int OCC>
-__global__ __launch_bounds__(256, OCC) void prefill_gemm_kernel(PrefillArgs a) {
+// A block holds 128 rows and 64 NJ weight rows.  GATEUP: h = silu(x Wg^T) *
+// (x Wu^T) for 128 rows x 32 NJ columns, plus the rows' partial sums of h
+// over those columns.  !GATEUP: y = h Wd^T for 128 rows x 64 NJ columns.  The
+// NW waves are (NW / WN) x WN over (rows x weight rows): a wave owns MI row
+// blocks of 32 and NJW weight-row blocks of 32 (gate/up: half gate, half up,
+// for the same columns), so every widened weight fragment feeds MI matrix-core
+// products and every staged activation byte feeds 64 NJ weight rows.  kNBuf
+// LDS stage buffers (kNBuf - 1 stages in flight); OCC blocks per compute unit.
+template <bool GATEUP, int NJ, int kNBuf, int OCC, int WN, int NW>
+__global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs a) {
+  constexpr int kThreads = 64 * NW;
   constexpr int kWRows = 64 * NJ;             // weight rows per block
   constexpr int kWBytes = kWRows * kWRow;
   constexpr int kStage = kABytes + kWBytes;
-  constexpr int kWI = NJ / 2;                 // weight-load instructions per wave per stage
-  static_assert(!GATEUP || NJ == 4, "gate/up blocks pair 2 gate and 2 up column blocks per wave");
+  constexpr int kAI = (kABytes / 1024) / NW;  // activation-load instructions (1 KB) per wave per stage
+  constexpr int kWI = (kWBytes / 1024) / NW;  // weight-load instructions per wave per stage
+  constexpr int WM = NW / WN;                 // waves along the rows
+  constexpr int MI = (kBM / 32) / WM;         // row blocks of 32 per wave
+  constexpr int NJW = (kWRows / 32) / WN;     // weight-row blocks of 32 per wave
+  static_assert(kAI * NW * 1024 == kABytes && kWI * NW * 1024 == kWBytes, "even copy split");
+  static_assert(WM * WN == NW && MI * WM * 32 == kBM && NJW * WN * 32 == kWRows, "wave grid");
+  static_assert(!GATEUP || NJW % 2 == 0, "gate/up waves pair gate and up column blocks");
   // One LDS object for the stage ring and the row sums: with several, the
   // compiler's alias information makes every LDS read wait for all
   // direct-to-LDS copies in flight (next stages included); the explicit
   // vmcnt waits below order the reads instead.
-  __shared__ __attribute__((aligned(1024))) char smem[kNBuf * kStage + 3 * kBM * 4];
+  __shared__ __attribute__((aligned(1024))) char smem[kNBuf * kStage + (1 + WN) * kBM * 4];
   float* rowsum = reinterpret_cast<float*>(smem + kNBuf * kStage);       // [kBM]
-  float (*hpart)[kBM] = reinterpret_cast<float (*)[kBM]>(rowsum + kBM);  // [2][kBM]
+  float (*hpart)[kBM] = reinterpret_cast<float (*)[kBM]>(rowsum + kBM);  // [WN][kBM]
   const int ntiles = *a.num_tiles;
   const int tile = blockIdx.y;
   if (tile >= ntiles) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, hh = lane >> 5;
   const int4 td = a.tiles[tile];  // (expert, slot, first grouped row, rows)
   const int slot = td.y, pbase = td.z, rows = td.w;
@@ -124,24 +147,24 @@ __global__ __launch_bounds__(256, OCC) void prefill_gemm_kernel(PrefillArgs a) {
   if (slot < 0 || slot >= a.num_slots) {
     if (tid == 0) atomicOr(a.flags, MOE_FLAG_BAD_SLOT);
     if (!GATEUP) {
-      for (int i = tid; i < rows * kWRows; i += 256)
+      for (int i = tid; i < rows * kWRows; i += kThreads)
         a.y[(size_t)(pbase + i / kWRows) * a.d + n0 + i % kWRows] = 0.0f;
     }
     return;
   }
   const size_t wrow_bytes = (size_t)K / 2;
 
-  // activation rows this lane copies: 16 instructions of 8 rows per stage, 4 per wave
-  const uint8_t* asrc[4];
+  // activation rows this lane copies: 16 instructions of 8 rows per stage, kAI per wave
+  const uint8_t* asrc[kAI];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = (wave * 4 + j) * 8 + lane / 8;
+  for (int j = 0; j < kAI; ++j) {
+    const int r = (wave * kAI + j) * 8 + lane / 8;
     const int rr = r < rows ? r : 0;
     const uint16_t* rowp = GATEUP ? a.act + (size_t)(a.perm[pbase + rr] / a.topk) * a.d
                                   : a.act + (size_t)(pbase + rr) * a.dff;
     asrc[j] = reinterpret_cast<const uint8_t*>(rowp) + 16 * apos(r, lane % 8);
   }
-  // weight rows: 2 NJ instructions of 32 rows per stage, NJ / 2 per wave
+  // weight rows: 2 NJ instructions of 32 rows per stage, kWI per wave
   const uint8_t* wsrc[kWI];
 #pragma unroll
   for (int j = 0; j < kWI; ++j) {
@@ -161,9 +184,16 @@ __global__ __launch_bounds__(256, OCC) void prefill_gemm_kernel(PrefillArgs a) {
       if (GATEUP) {
         v = a.xsum[a.perm[pbase + tid] / a.topk];
       } else {
-        const int nparts = a.dff / 128;
-        const float* hp = a.hsum_part + (size_t)(pbase + tid) * nparts;
-        for (int i = 0; i < nparts; ++i) v += hp[i];
+        const float* hp = a.hsum_part + (size_t)(pbase + tid) * a.hparts;
+        int i = 0;
+        for (; i + 8 <= a.hparts; i += 8) {  // 8 loads in flight
+          float t[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) t[u] = hp[i + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v += t[u];
+        }
+        for (; i < a.hparts; ++i) v += hp[i];
       }
     }
     rowsum[tid] = v;
@@ -172,95 +202,109 @@ __global__ __launch_bounds__(256, OCC) void prefill_gemm_kernel(PrefillArgs a) {
   auto issue = [&](int st) {
     char* buf = smem + (st % kNBuf) * kStage;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_lds16(asrc[j] + (size_t)st * kARow, buf + (wave * 4 + j) * 1024);
+    for (int j = 0; j < kAI; ++j) load_lds16(asrc[j] + (size_t)st * kARow, buf + (wave * kAI + j) * 1024);
 #pragma unroll
     for (int j = 0; j < kWI; ++j)
       load_lds16(wsrc[j] + (size_t)st * kWRow, buf + kABytes + (wave * kWI + j) * 1024);
   };
 
-  f32x16 acc[2][NJ];
+  f32x16 acc[MI][NJW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
-  // this wave's weight rows: gate/up -> gate 64wn + 32j (j < 2) and up 128 + 64wn + 32(j-2);
-  // down -> 32 NJ wn + 32j
-  int wr[NJ];
+    for (int j = 0; j < NJW; ++j) acc[i][j] = f32x16{};
+  // this wave's weight rows: gate/up -> gate 16 NJW wn + 32j (j < NJW/2) and
+  // up kWRows/2 + 16 NJW wn + 32(j - NJW/2); down -> 32 NJW wn + 32j
+  constexpr int HJ = NJW / 2;
+  int wr[NJW];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
-    wr[j] = GATEUP ? (j < 2 ? 64 * wn + 32 * j : kWRows / 2 + 64 * wn + 32 * (j - 2)) : 32 * NJ * wn + 32 * j;
+  for (int j = 0; j < NJW; ++j)
+    wr[j] = GATEUP ? (j < HJ ? 32 * HJ * wn + 32 * j : kWRows / 2 + 32 * HJ * wn + 32 * (j - HJ)) : 32 * NJW * wn + 32 * j;
 
   const int nst = K / kBK;
 #pragma unroll
   for (int st = 0; st < kNBuf - 1; ++st)
     if (st < nst) issue(st);
   for (int st = 0; st < nst; ++st) {
-    if (st + kNBuf - 1 < nst) issue(st + kNBuf - 1);
-    // wait until stage st has landed: the stages issued after it may stay in flight
-    const int later = min(kNBuf - 1, nst - 1 - st);
-    if (kNBuf > 3 && later >= 3)
-      wait_vmem<(kNBuf > 3 ? 3 : 0) * (4 + kWI)>();
-    else if (kNBuf > 2 && later >= 2)
-      wait_vmem<(kNBuf > 2 ? 2 : 0) * (4 + kWI)>();
-    else if (later >= 1)
-      wait_vmem<4 + kWI>();
+    // wait until stage st has landed (the later stages issued so far -- at
+    // most kNBuf - 2 -- may stay in flight), then a barrier: every wave is
+    // past stage st - 1, so its buffer can be refilled with stage st + kNBuf - 1
+    const int later = min(kNBuf - 2, nst - 1 - st);
+    if (kNBuf > 3 && later >= 2)
+      wait_vmem<(kNBuf > 3 ? 2 : 0) * (kAI + kWI)>();
+    else if (kNBuf > 2 && later >= 1)
+      wait_vmem<(kNBuf > 2 ? 1 : 0) * (kAI + kWI)>();
     else
       wait_vmem<0>();
     lds_barrier();
+    if (st + kNBuf - 1 < nst) issue(st + kNBuf - 1);
     const char* buf = smem + (st % kNBuf) * kStage;
-    u32x4 bq[NJ];
+    u32x4 bq[NJW];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+    for (int j = 0; j < NJW; ++j) {
       const int r = wr[j] + l32;
       bq[j] = *reinterpret_cast<const u32x4*>(buf + kABytes + r * kWRow + 16 * wpos(r, hh));
     }
+    // A fragments (fragment order already) of step s; the next step's are read
+    // before this step's products, so the LDS latency hides behind them
+    auto read_a = [&](int s, u32x4(&av)[MI]) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = 32 * MI * wm + 32 * i + l32;
+        av[i] = *reinterpret_cast<const u32x4*>(buf + r * kARow + 16 * apos(r, 4 * hh + s));
+      }
+    };
+    u32x4 av0[MI], av1[MI];
+    read_a(0, av0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4 av[2];
+      u32x4(&cur)[MI] = (s & 1) ? av1 : av0;
+      u32x4(&nxt)[MI] = (s & 1) ? av0 : av1;
+      if (s + 1 < 4) read_a(s + 1, nxt);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = 64 * wm + 32 * i + l32;
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(buf + r * kARow + 16 * apos(r, 4 * hh + s));
-        av[i] = raw;  // x and h are stored in fragment order already
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
+      for (int j = 0; j < NJW; ++j) {
         const u32x4 b = codes_to_bf16(bq[j][s]);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) acc[i][j] = mfma32(av[i], b, acc[i][j]);
+        for (int i = 0; i < MI; ++i) acc[i][j] = mfma32(cur[i], b, acc[i][j]);
       }
     }
-    lds_barrier();
   }
 
-  // epilogue; accumulator element e of lane l is row 8(e/4) + 4(l/32) + e%4, column l%32
+  // epilogue; accumulator element e of lane l is row 8(e/4) + 4(l/32) + e%4, column l%32.
+  // Results go through LDS (the stage ring is free once every wave is past
+  // its last stage), so that global memory sees whole-row 16-byte stores.
+  // The barriers here wait for LDS only: a store has read its data out of LDS
+  // once issued, and nothing here reads global memory the stores write.
+  lds_barrier();
   if (GATEUP) {
-    float psum[2][16];
+    constexpr int kCols = kWRows / 2;  // output columns of the block
+    static_assert(kBM * kCols * 2 <= kNBuf * kStage, "h tile fits the stage ring");
+    uint16_t* htile = reinterpret_cast<uint16_t*>(smem);  // [kBM][kCols], columns in h_phys_col order
+    float psum[MI][16];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int n = n0 + 64 * wn + 32 * jj + l32;
-      const size_t sidx = (size_t)slot * ncols + n;
+    for (int jj = 0; jj < HJ; ++jj) {
+      const int nl = 32 * HJ * wn + 32 * jj + l32;  // column inside the block (n0 is a multiple of 8)
+      const size_t sidx = (size_t)slot * ncols + n0 + nl;
       const float sg = fp16_to_f32(a.s0[sidx]), cg = kCodeBias + fp16_to_f32(a.z0[sidx]);
       const float su = fp16_to_f32(a.s1[sidx]), cu = kCodeBias + fp16_to_f32(a.z1[sidx]);
-      const int hcol = h_phys_col(n);
+      const int hcol = h_phys_col(nl);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = 64 * wm + 32 * i + 8 * (e / 4) + 4 * hh + (e % 4);
+          const int row = 32 * MI * wm + 32 * i + 8 * (e / 4) + 4 * hh + (e % 4);
           const float xs = rowsum[row];
           const float g = sg * (acc[i][jj][e] - cg * xs);
-          const float u = su * (acc[i][jj + 2][e] - cu * xs);
+          const float u = su * (acc[i][jj + HJ][e] - cu * xs);
           const uint16_t hb = f32_to_bf16(silu(g) * u);
-          const float hv = bf16_to_f32(hb);
-          psum[i][e] = (jj == 0 ? 0.0f : psum[i][e]) + hv;
-          if (row < rows) a.h[(size_t)(pbase + row) * a.dff + hcol] = hb;
+          psum[i][e] = (jj == 0 ? 0.0f : psum[i][e]) + bf16_to_f32(hb);
+          htile[row * kCols + hcol] = hb;
         }
       }
     }
-    // sum each row's partials over the 32 lanes holding its columns, then over the 2 waves
+    // sum each row's partials over the 32 lanes holding its columns, then over the WN waves
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float v = psum[i][e];
@@ -270,30 +314,79 @@ __global__ __launch_bounds__(256, OCC) void prefill_gemm_kernel(PrefillArgs a) {
       }
     if (l32 == 0) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) hpart[wn][64 * wm + 32 * i + 8 * (e / 4) + 4 * hh + (e % 4)] = psum[i][e];
+        for (int e = 0; e < 16; ++e) hpart[wn][32 * MI * wm + 32 * i + 8 * (e / 4) + 4 * hh + (e % 4)] = psum[i][e];
     }
-    __syncthreads();
-    if (tid < rows && tid < kBM)
-      a.hsum_part[(size_t)(pbase + tid) * (a.dff / 128) + blockIdx.x] = hpart[0][tid] + hpart[1][tid];
+    lds_barrier();
+    constexpr int kChunks = kCols / 8;  // 16-byte chunks per row
+    for (int c = tid; c < rows * kChunks; c += kThreads) {
+      const int r = c / kChunks, q = c % kChunks;
+      *reinterpret_cast<u32x4*>(a.h + (size_t)(pbase + r) * a.dff + n0 + 8 * q) =
+          *reinterpret_cast<const u32x4*>(htile + r * kCols + 8 * q);
+    }
+    if (tid < rows && tid < kBM) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) v += hpart[w][tid];
+      a.hsum_part[(size_t)(pbase + tid) * a.hparts + blockIdx.x] = v;
+    }
+  } else if constexpr (WM == 1) {
+    // one pass per 32-row block: every wave holds all rows of the block
+    static_assert(32 * kWRows * 4 <= kNBuf * kStage, "y tile fits the stage ring");
+    float* ytile = reinterpret_cast<float*>(smem);  // [32][kWRows]
+    float sd[NJW], cd[NJW];
+#pragma unroll
+    for (int j = 0; j < NJW; ++j) {
+      const size_t sidx = (size_t)slot * ncols + n0 + 32 * NJW * wn + 32 * j + l32;
+      sd[j] = fp16_to_f32(a.s0[sidx]);
+      cd[j] = kCodeBias + fp16_to_f32(a.z0[sidx]);
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      if (32 * i >= rows) break;
+#pragma unroll
+      for (int j = 0; j < NJW; ++j) {
+        const int nl = 32 * NJW * wn + 32 * j + l32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int rl = 8 * (e / 4) + 4 * hh + (e % 4);
+          ytile[rl * kWRows + nl] = sd[j] * (acc[i][j][e] - cd[j] * rowsum[32 * i + rl]);
+        }
+      }
+      lds_barrier();
+      constexpr int kChunks = kWRows / 4;  // 16-byte chunks per row
+      const int nr = min(32, rows - 32 * i);
+      for (int c = tid; c < nr * kChunks; c += kThreads) {
+        const int r = c / kChunks, q = c % kChunks;
+        *reinterpret_cast<float4*>(a.y + (size_t)(pbase + 32 * i + r) * a.d + n0 + 4 * q) =
+            *reinterpret_cast<const float4*>(ytile + r * kWRows + 4 * q);
+      }
+      lds_barrier();
+    }
   } else {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int n = n0 + 32 * NJ * wn + 32 * j + l32;
+    for (int j = 0; j < NJW; ++j) {
+      const int n = n0 + 32 * NJW * wn + 32 * j + l32;
       const size_t sidx = (size_t)slot * ncols + n;
       const float sd = fp16_to_f32(a.s0[sidx]), cd = kCodeBias + fp16_to_f32(a.z0[sidx]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = 64 * wm + 32 * i + 8 * (e / 4) + 4 * hh + (e % 4);
+          const int row = 32 * MI * wm + 32 * i + 8 * (e / 4) + 4 * hh + (e % 4);
           if (row < rows) a.y[(size_t)(pbase + row) * a.d + n] = sd * (acc[i][j][e] - cd * rowsum[row]);
         }
       }
     }
   }
 }
+
+namespace {
+// gate/up blocks are 32 NJ output columns wide: the wide block when d_ff allows it
+bool gateup_wide(const moe_config& c) { return c.d_ff % (32 * kPrefillGateUpNJ) == 0; }
+int gateup_blocks(const moe_config& c) { return c.d_ff / (gateup_wide(c) ? 32 * kPrefillGateUpNJ : 128); }
+}  // namespace
 
 void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w,
                            char* ws, hipStream_t s) {
@@ -317,8 +410,13 @@ void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* h
   a.z1 = w.z_up;
   a.h = reinterpret_cast<uint16_t*>(ws + p.h);
   a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
-  dim3 grid(c.d_ff / 128, p.max_tiles);
-  prefill_gemm_kernel<true, 4, kPrefillGateUpStages, kPrefillGateUpBlocks><<<grid, 256, 0, s>>>(a);
+  a.hparts = gateup_blocks(c);
+  dim3 grid(a.hparts, p.max_tiles);
+  if (gateup_wide(c))
+    prefill_gemm_kernel<true, kPrefillGateUpNJ, kPrefillGateUpStages, kPrefillGateUpBlocks, kPrefillGateUpWaves,
+                        kPrefillGateUpWaves><<<grid, 64 * kPrefillGateUpWaves, 0, s>>>(a);
+  else
+    prefill_gemm_kernel<true, 4, 2, 2, 4, 4><<<grid, 256, 0, s>>>(a);
 }
 
 void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& w, char* ws, hipStream_t s) {
@@ -327,6 +425,7 @@ void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& 
   a.tiles = reinterpret_cast<const int4*>(ws + p.tiles);
   a.num_tiles = reinterpret_cast<const int32_t*>(ws + p.num_tiles);
   a.hsum_part = reinterpret_cast<float*>(ws + p.hsum_part);
+  a.hparts = gateup_blocks(c);
   a.num_slots = c.num_slots;
   a.d = c.d_model;
   a.dff = c.d_ff;
@@ -337,9 +436,10 @@ void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& 
   a.y = reinterpret_cast<float*>(ws + p.y);
   a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
   if (c.d_model % 256 == 0) {
-    prefill_gemm_kernel<false, 4, kPrefillDownStages, kPrefillDownBlocks><<<dim3(c.d_model / 256, p.max_tiles), 256, 0, s>>>(a);
+    prefill_gemm_kernel<false, 4, kPrefillDownStages, kPrefillDownBlocks, kPrefillDownWaves, kPrefillDownWaves>
+        <<<dim3(c.d_model / 256, p.max_tiles), 64 * kPrefillDownWaves, 0, s>>>(a);
   } else {
-    prefill_gemm_kernel<false, 2, 2, 2><<<dim3(c.d_model / 128, p.max_tiles), 256, 0, s>>>(a);
+    prefill_gemm_kernel<false, 2, 2, 2, 2, 4><<<dim3(c.d_model / 128, p.max_tiles), 256, 0, s>>>(a);
   }
 }
 
