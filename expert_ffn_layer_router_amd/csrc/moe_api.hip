@@ -94,9 +94,10 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   if (T <= kStreamMaxTokens) {
     p->router_split = 0;
   } else {
-    // 64 x 64 tiles; split k (in multiples of 32) until about 256 blocks
-    const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
-    p->router_split = largest_divisor_at_most(c.d_model / 32, std::max(1, (256 + tiles - 1) / tiles));
+    // 64-token x router_tile_experts(E) tiles; split k (in multiples of 32) until about 512 blocks
+    const int tiles = ((T + kRouterMfmaTokens - 1) / kRouterMfmaTokens) *
+                      ((E + router_tile_experts(E) - 1) / router_tile_experts(E));
+    p->router_split = largest_divisor_at_most(c.d_model / kRouterMfmaK, std::max(1, (512 + tiles - 1) / tiles));
   }
   // GEMM row tiles: sum_e ceil(c_e / rows) <= ceil(R / rows) + (non-empty experts)
   p->max_tiles = (p->R + p->tile_rows - 1) / p->tile_rows + std::min(E, p->R);

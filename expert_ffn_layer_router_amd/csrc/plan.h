@@ -12,6 +12,10 @@
 namespace moe {
 
 constexpr int kRouterTokTile = 16;     // tokens per router wave
+constexpr int kRouterMfmaTokens = 64;  // many-token router: tokens per block tile (16 per wave)
+constexpr int kRouterMfmaK = 32;       // many-token router: k per LDS chunk
+// many-token router: experts per block tile (a multiple of 16, the MFMA width)
+inline int router_tile_experts(int E) { return E > 32 ? 64 : (E > 16 ? 32 : 16); }
 constexpr int kPrefillTileRows = 128;  // prefill family: rows of an expert group per GEMM tile
 constexpr int kGemmKStep = 128;        // granularity of the decode down GEMM's k-split
 constexpr int kPermuteThreads = 1024;

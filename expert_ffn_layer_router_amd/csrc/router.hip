@@ -229,68 +229,86 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
   if (threadIdx.x == 0) reset_ticket(ticket);
 }
 
-// Many tokens: an fp64 GEMM tile of 64 tokens x 64 experts per block over one
-// k-split; operands are widened to fp64 once, in LDS, and every thread owns a
-// 4 x 4 block of logits.  Output: logits[split][t][e], summed in split order
-// by router_topk_kernel.
-constexpr int kRtTok = 64, kRtExp = 64, kRtK = 32;
-
-__global__ __launch_bounds__(256) void router_logits_tiled_kernel(const uint16_t* __restrict__ hidden,
-                                                                  const float* __restrict__ wr,
-                                                                  double* __restrict__ logits, int T, int d,
-                                                                  int E, int kchunk) {
-  __shared__ double xs[kRtK][kRtTok];
-  __shared__ double ws[kRtK][kRtExp];
-  const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;  // tokens 4ty.., experts 4tx..
-  const int t0 = blockIdx.x * kRtTok, e0 = blockIdx.y * kRtExp, split = blockIdx.z;
-  const int kbeg = split * kchunk;
-  double acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  for (int kc = kbeg; kc < kbeg + kchunk; kc += kRtK) {
-    for (int i = tid; i < kRtTok * kRtK; i += 256) {
-      const int r = i / kRtK, c = i % kRtK;
-      const int t = t0 + r;
-      xs[c][r] = (t < T) ? (double)bf16_to_f32(hidden[(size_t)t * d + kc + c]) : 0.0;
+// Many tokens: the logits as an fp64 GEMM on the matrix cores
+// (v_mfma_f64_16x16x4_f64).  The products bf16 x fp32 are exact in fp64 and
+// every logit is summed by the same sequence of fp64 operations (k in steps
+// of 4 inside the matrix core, then the k-splits in order), so exact ties
+// still go to the lower expert id.  A block computes 64 tokens x TN experts
+// over one k-split; each wave 16 tokens x TN experts.  Chunks of 32 k are
+// loaded into registers one chunk ahead, widened to fp64 and stored k-major
+// in LDS, where each MFMA operand is one conflict-free ds_read_b64 (lane l:
+// A = x[t0 + l % 16][k + l / 16], B = W[e0 + l % 16][k + l / 16]; D element
+// r of lane l is (token l / 16 + 4 r, expert l % 16)).  Output:
+// logits[split][t][e], summed in split order by router_topk_kernel.
+template <int TN>
+__global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t* __restrict__ hidden,
+                                                                 const float* __restrict__ wr,
+                                                                 double* __restrict__ logits, int T, int d, int E,
+                                                                 int kchunk) {
+  constexpr int TM = kRouterMfmaTokens, KC = kRouterMfmaK, NB = TN / 16;
+  __shared__ double xs[KC][TM];
+  __shared__ double wsh[KC][TN];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * TM, e0 = blockIdx.y * TN, split = blockIdx.z;
+  const int kbeg = split * kchunk, kend = kbeg + kchunk;
+  // staging: thread -> x row t0 + tid % 64, k 8 (tid / 64) .. +8 of the chunk;
+  // W row e0 + tid % TN (the first 4 TN threads: 8 k each)
+  const int xr = tid % TM, xk = 8 * (tid / TM);
+  const bool xok = t0 + xr < T;
+  const uint16_t* xsrc = hidden + (size_t)(xok ? t0 + xr : 0) * d + xk;
+  const int wrow = tid % TN, wk = 8 * (tid / TN);
+  const bool wact = tid < 4 * TN, wok = wact && e0 + wrow < E;
+  const float* wsrc = wr + (size_t)(wok ? e0 + wrow : 0) * d + (wact ? wk : 0);
+  u32x4 xv;
+  float4 w0, w1;
+  auto fetch = [&](int kc) {
+    xv = *reinterpret_cast<const u32x4*>(xsrc + kc);
+    if (wact) {
+      w0 = *reinterpret_cast<const float4*>(wsrc + kc);
+      w1 = *reinterpret_cast<const float4*>(wsrc + kc + 4);
     }
-    for (int i = tid; i < kRtExp * kRtK; i += 256) {
-      const int r = i / kRtK, c = i % kRtK;
-      const int e = e0 + r;
-      ws[c][r] = (e < E) ? (double)wr[(size_t)e * d + kc + c] : 0.0;
+  };
+  auto stage = [&]() {
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xs[xk + 2 * i][xr] = xok ? (double)__uint_as_float(xw[i] << 16) : 0.0;
+      xs[xk + 2 * i + 1][xr] = xok ? (double)__uint_as_float(xw[i] & 0xFFFF0000u) : 0.0;
     }
+    if (wact) {
+      const float wf[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wsh[wk + i][wrow] = wok ? (double)wf[i] : 0.0;
+    }
+  };
+  f64x4 acc[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) acc[n] = f64x4{0.0, 0.0, 0.0, 0.0};
+  fetch(kbeg);
+  for (int kc = kbeg; kc < kend; kc += KC) {
+    __syncthreads();  // the previous chunk's operands are read
+    stage();
     __syncthreads();
-#pragma unroll 4
-    for (int c = 0; c < kRtK; ++c) {
-      double a[4], b[4];
+    if (kc + KC < kend) fetch(kc + KC);  // next chunk's loads in flight during the products
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = xs[c][4 * ty + i];
+    for (int k4 = 0; k4 < KC; k4 += 4) {
+      const double av = xs[k4 + lane / 16][16 * wave + lane % 16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = ws[c][4 * tx + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+      for (int n = 0; n < NB; ++n) {
+        const double bv = wsh[k4 + lane / 16][16 * n + lane % 16];
+        acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[n], 0, 0, 0);
+      }
     }
-    __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + 4 * ty + i;
-    if (t >= T) continue;
+  for (int n = 0; n < NB; ++n)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + 4 * tx + j;
-      if (e < E) logits[((size_t)split * T + t) * E + e] = acc[i][j];
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 16 * wave + lane / 16 + 4 * r, e = e0 + 16 * n + lane % 16;
+      if (t < T && e < E) logits[((size_t)split * T + t) * E + e] = acc[n][r];
     }
-  }
 }
 
-// One wave per token (many-token path): top-k, and the token's row sum
-// sum_k x[t][k] (fp64, rounded to fp32) that the prefill gate/up GEMM's
-// zero-point term needs.  Also clears the device error flags of this forward.
 __global__ __launch_bounds__(256) void router_topk_kernel(const double* __restrict__ logits, int nsplit,
                                                           const float* __restrict__ bias,
                                                           const uint16_t* __restrict__ hidden, int d, int T,
@@ -332,9 +350,15 @@ void launch_router(const moe_config& c, const Plan& p, const uint16_t* hidden, c
                                              regroup_args(c, p, slot_table, ws));
     return;
   }
-  dim3 grid((p.T + kRtTok - 1) / kRtTok, (c.num_experts + kRtExp - 1) / kRtExp, p.router_split);
-  router_logits_tiled_kernel<<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, c.num_experts,
-                                                  c.d_model / p.router_split);
+  const int tn = router_tile_experts(c.num_experts);
+  dim3 grid((p.T + kRouterMfmaTokens - 1) / kRouterMfmaTokens, (c.num_experts + tn - 1) / tn, p.router_split);
+  const int kchunk = c.d_model / p.router_split;
+  if (tn == 64)
+    router_logits_mfma_kernel<64><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, c.num_experts, kchunk);
+  else if (tn == 32)
+    router_logits_mfma_kernel<32><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, c.num_experts, kchunk);
+  else
+    router_logits_mfma_kernel<16><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, c.num_experts, kchunk);
   router_topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(logits, p.router_split, router_bias, hidden, c.d_model, p.T,
                                                    c.num_experts, c.top_k, topk_idx, topk_w,
                                                    reinterpret_cast<float*>(ws + p.xsum),
