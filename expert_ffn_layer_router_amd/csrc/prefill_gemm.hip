@@ -100,7 +100,7 @@ struct PrefillArgs {
   const uint8_t* w1;          // up codes
   const uint16_t *s0, *z0, *s1, *z1;
   uint16_t* h;                // gate/up output [R][dff], fragment k-order
-  float* y;                   // down output [R][d]
+  uint16_t* y;                // down output [R][d], bf16
   uint32_t* flags;
 };
 
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
     if (tid == 0) atomicOr(a.flags, MOE_FLAG_BAD_SLOT);
     if (!GATEUP) {
       for (int i = tid; i < rows * kWRows; i += kThreads)
-        a.y[(size_t)(pbase + i / kWRows) * a.d + n0 + i % kWRows] = 0.0f;
+        a.y[(size_t)(pbase + i / kWRows) * a.d + n0 + i % kWRows] = 0;
     }
     return;
   }
@@ -355,12 +355,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
         }
       }
       lds_barrier();
-      constexpr int kChunks = kWRows / 4;  // 16-byte chunks per row
+      constexpr int kChunks = kWRows / 8;  // 8 columns -> one 16-byte bf16 store
       const int nr = min(32, rows - 32 * i);
       for (int c = tid; c < nr * kChunks; c += kThreads) {
         const int r = c / kChunks, q = c % kChunks;
-        *reinterpret_cast<float4*>(a.y + (size_t)(pbase + 32 * i + r) * a.d + n0 + 4 * q) =
-            *reinterpret_cast<const float4*>(ytile + r * kWRows + 4 * q);
+        const float4 v0 = *reinterpret_cast<const float4*>(ytile + r * kWRows + 8 * q);
+        const float4 v1 = *reinterpret_cast<const float4*>(ytile + r * kWRows + 8 * q + 4);
+        u32x4 o;
+        o.x = (uint32_t)f32_to_bf16(v0.x) | ((uint32_t)f32_to_bf16(v0.y) << 16);
+        o.y = (uint32_t)f32_to_bf16(v0.z) | ((uint32_t)f32_to_bf16(v0.w) << 16);
+        o.z = (uint32_t)f32_to_bf16(v1.x) | ((uint32_t)f32_to_bf16(v1.y) << 16);
+        o.w = (uint32_t)f32_to_bf16(v1.z) | ((uint32_t)f32_to_bf16(v1.w) << 16);
+        *reinterpret_cast<u32x4*>(a.y + (size_t)(pbase + 32 * i + r) * a.d + n0 + 8 * q) = o;
       }
       lds_barrier();
     }
@@ -375,7 +381,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = 32 * MI * wm + 32 * i + 8 * (e / 4) + 4 * hh + (e % 4);
-          if (row < rows) a.y[(size_t)(pbase + row) * a.d + n] = sd * (acc[i][j][e] - cd * rowsum[row]);
+          if (row < rows) a.y[(size_t)(pbase + row) * a.d + n] = f32_to_bf16(sd * (acc[i][j][e] - cd * rowsum[row]));
         }
       }
     }
@@ -433,7 +439,7 @@ void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& 
   a.w0 = w.w_down;
   a.s0 = w.s_down;
   a.z0 = w.z_down;
-  a.y = reinterpret_cast<float*>(ws + p.y);
+  a.y = reinterpret_cast<uint16_t*>(ws + p.y);
   a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
   if (c.d_model % 256 == 0) {
     prefill_gemm_kernel<false, 4, kPrefillDownStages, kPrefillDownBlocks, kPrefillDownWaves, kPrefillDownWaves>
