@@ -6,18 +6,28 @@
 // with their own scale and zero-point, dequantised on the load path.
 //
 // A block owns one row tile of one expert (up to 16 rows of its group) and
-// 64 x NCW output columns; each of its 4 waves computes 16 x NCW of them.  The
-// k range is walked in stages of kStageK: per stage the block copies 128 bytes
-// of every weight row it needs (gate and up rows, or down rows) and 512 bytes
-// of every activation row straight from HBM into LDS (global_load_lds_dwordx4,
-// full 128-byte lines, several rows per instruction) into one of two
-// buffers, so the next stage is in flight while one is multiplied; activation
-// rows past the tile's end are not copied.  Wider blocks (NCW = 2) halve the
-// activation bytes staged per weight byte.  The 16-byte
-// chunks are XOR-swizzled in LDS so that the MFMA fragment reads are free of
-// bank conflicts.  Codes are widened to bf16 in registers (codes_to_bf16) and
-// the scale / zero-point are applied in the epilogue; the row sums of A the
-// zero-point term needs come from one extra MFMA against a B of ones.
+// 64 x NCW output columns, and walks its k range in stages of kStageK.  Per
+// stage it copies 128 bytes of every weight row it needs (gate and up rows,
+// or down rows) straight from HBM into LDS (global_load_lds_dwordx4, full
+// 128-byte lines, 8 rows per instruction) into a ring of NBUF buffers, so
+// the next stages are in flight while one is multiplied.  The 16-byte chunks
+// are XOR-swizzled in LDS so that the MFMA fragment reads spread over the
+// banks.
+//
+// The four waves split each stage's k range into KW parts and the block's
+// columns into 4 / KW parts (wave w takes k part kp = w % KW and column part
+// cp = w / KW).  Each wave loads its activation fragments straight from L2
+// into registers, one stage ahead: per MFMA k-step 16 contiguous bytes of
+// one row per lane.  The LDS thus holds weights only (2 x 16 KB for gate/up,
+// 2 x 8 KB for down at NCW = 1), so more blocks -- and more weight bytes in
+// flight -- fit on a CU than if the activations were staged there too; with
+// KW = 4 no two waves load the same activation bytes.
+//
+// Codes are widened to bf16 in registers (codes_to_bf16); the row sums of A
+// that the zero-point term needs come from one extra MFMA against a B of
+// ones.  At the end every wave turns its k part into s (acc - (128 + z) sum a),
+// which is linear in the k parts, and the parts are added in a fixed order
+// through LDS by the wave that owns each column tile, which also stores it.
 //
 // With few tokens the weighted scatter-back (combine) is fused into the down
 // kernel: the last block to finish a 64-column slice (an atomic ticket per
@@ -32,16 +42,19 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kStageK = 256;                  // k per stage
 constexpr int kWRowBytes = kStageK / 2;       // int4 bytes of one weight row per stage
-constexpr int kARowBytes = kStageK * 2;       // bf16 bytes of one activation row per stage
 constexpr int kRowsPerWInst = 1024 / kWRowBytes;  // weight rows per 1 KB load instruction (8)
-constexpr int kRowsPerAInst = 1024 / kARowBytes;  // activation rows per instruction (2)
 
 // 16 bytes from global memory to LDS: lane l of the wave writes lds_base + 16 l.
+// NT: with the non-temporal hint, for lines read once per launch: they are
+// marked for early eviction, so streaming them leaves the caches to the
+// activations and to the next kernels' inputs.
+template <bool NT>
 __device__ __forceinline__ void load_lds16(const void* g, char* lds_base) {
-  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds_base, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds_base, 16, 0, NT ? 2 /* nt */ : 0);
 }
 
 // Wait until at most `n` vector-memory operations of this wave are pending.
@@ -54,15 +67,15 @@ __device__ __forceinline__ void wait_vmem() {
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also orders global
 // memory, which makes the compiler wait for every outstanding global load --
-// including the next stage's copies, defeating the double buffering.  The LDS
-// copies of a stage are waited for explicitly (wait_vmem) before this.
+// including the next stages' copies, defeating the ring.  The LDS copies of a
+// stage are waited for explicitly (wait_vmem) before this.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // LDS reads written as inline assembly.  The compiler treats a plain LDS read
 // as depending on every direct-to-LDS copy still in flight (it cannot tell
-// the two stage buffers apart) and waits for all of them, next stage included,
+// the ring's buffers apart) and waits for all of them, later stages included,
 // which would serialise the copy pipeline.  These reads are ordered by the
 // explicit waits and barriers instead: lds_wait() waits for the wave's LDS
 // reads, and lds_ready(v) makes each value depend on that wait, so no use of
@@ -73,24 +86,17 @@ __device__ __forceinline__ u32x4 lds_read16(const char* p) {
   asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
   return v;
 }
-__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void lds_ready(u32x4& v) { asm volatile("" : "+v"(v)); }
-
-// Swizzled 16-byte chunk positions inside a stage buffer.
-__device__ __forceinline__ int wchunk_pos(int row, int c) { return c ^ ((row >> 1) & 7); }  // c < 8
-__device__ __forceinline__ int achunk_pos(int row, int q) { return q ^ (row & 15); }         // q < 32
-
-// wait_vmem with a run-time count n in [BASE, BASE + EXTRA]
-template <int BASE, int EXTRA>
-__device__ __forceinline__ void wait_vmem_rt(int n) {
-  if constexpr (EXTRA > 0) {
-    if (n > BASE) {
-      wait_vmem_rt<BASE + 1, EXTRA - 1>(n);
-      return;
-    }
-  }
-  wait_vmem<BASE>();
+__device__ __forceinline__ u32x2 lds_read8(const char* p) {
+  u32x2 v;
+  const uint32_t addr = (uint32_t)(uintptr_t)(const lds_void*)p;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
 }
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_ready(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
+// Swizzled position of 16-byte chunk c (< 8) of weight row `row` in a stage buffer.
+__device__ __forceinline__ int wchunk_pos(int row, int c) { return c ^ ((row >> 1) & 7); }
 
 }  // namespace
 
@@ -117,193 +123,15 @@ struct StreamArgs {
   FusedCombine fc;
 };
 
-// GATEUP: h rows of one tile, silu(x Wg^T) * (x Wu^T) in bf16, columns of
-// every group of 8 in the fragment k-order (h_phys_col).
-// !GATEUP: ypart[split][p] = h[p] Wd^T over the k range of `split`, fp32,
-// written with coherent stores; with a FusedCombine, the last block of each
-// column slice also writes that slice of out[].
-template <bool GATEUP, int NCW>
-__global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
-  constexpr int COLS = 64 * NCW;                        // output columns per block
-  constexpr int NWR = (GATEUP ? 2 : 1) * COLS;          // weight rows per stage
-  constexpr int WBYTES = NWR * kWRowBytes, ABYTES = kStreamTileRows * kARowBytes;
-  constexpr int SBYTES = WBYTES + ABYTES;
-  constexpr int WI = NWR / kRowsPerWInst / 4;           // weight-load instructions per wave per stage
-  constexpr int AI = kStreamTileRows / kRowsPerAInst / 4;  // activation-load instructions per wave per stage
-  static_assert(WI * kRowsPerWInst * 4 == NWR && AI * kRowsPerAInst * 4 == kStreamTileRows, "even split over waves");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * SBYTES];
+// Fused combine: the last block to finish a column slice (an atomic ticket
+// per slice) gathers that slice of out[] for every token: per token the k
+// routed rows in order j = 0..k-1, each the fixed-order sum of its k-splits.
+template <int COLS>
+__device__ void fused_combine_tail(const StreamArgs& a, int bx, int ntiles) {
   __shared__ int is_last;
-
-  const int ntiles = *a.num_tiles;
-  const int tile = blockIdx.y;
-  if (tile >= ntiles) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * COLS;
-  const int4 td = a.tiles[tile];  // (expert, slot, first grouped row, rows <= 16)
-  const int slot = td.y, pbase = td.z, rows = td.w;
-  const int ncols_total = GATEUP ? a.dff : a.d;   // output columns of this GEMM
-  const int K = GATEUP ? a.d : a.kchunk;          // k range of this block
-  const int kbeg = GATEUP ? 0 : blockIdx.z * a.kchunk;
-  const size_t row_bytes = (size_t)(GATEUP ? a.d : a.dff) / 2;
-  const bool bad = slot < 0 || slot >= a.num_slots;
-  float* yrow = GATEUP ? nullptr : a.ypart + ((size_t)blockIdx.z * a.R + pbase) * a.d;
-
-  if (bad) {
-    if (threadIdx.x == 0) atomicOr(a.flags, MOE_FLAG_BAD_SLOT);
-    if (GATEUP) return;
-#pragma unroll
-    for (int cb = 0; cb < NCW; ++cb) {
-      const int n = n0 + wave * 16 * NCW + cb * 16 + lr;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (grp * 4 + i < rows) store_coherent(&yrow[(size_t)(grp * 4 + i) * a.d + n], 0.0f);
-    }
-  } else {
-    // activation row sources (gate/up: tokens through perm -- dependent loads first)
-    int arow[AI];
-#pragma unroll
-    for (int j = 0; j < AI; ++j) {
-      const int m = (wave * AI + j) * kRowsPerAInst + lane / 32;
-      const int mm = m < rows ? m : 0;
-      arow[j] = GATEUP ? a.perm[pbase + mm] : pbase + mm;
-    }
-    const uint8_t* wsrc[WI];
-#pragma unroll
-    for (int j = 0; j < WI; ++j) {
-      const int r = (wave * WI + j) * kRowsPerWInst + lane / 8;  // block weight row
-      const uint8_t* base = (!GATEUP || r < COLS) ? a.w0 : a.w1;
-      const int n = n0 + (r % COLS);
-      wsrc[j] = base + ((size_t)slot * ncols_total + n) * row_bytes + kbeg / 2 + 16 * wchunk_pos(r, lane % 8);
-    }
-    const int nst = (K + kStageK - 1) / kStageK;
-    const bool half_last = (K % kStageK) != 0;
-    auto issue_w = [&](int st) {
-      char* buf = smem + (st & 1) * SBYTES;
-      const bool half = half_last && st == nst - 1;
-#pragma unroll
-      for (int j = 0; j < WI; ++j) {
-        const int r = (wave * WI + j) * kRowsPerWInst + lane / 8;
-        if (!half || wchunk_pos(r, lane % 8) < 4)  // global chunk < 4: k inside the half stage
-          load_lds16(wsrc[j] + (size_t)st * kWRowBytes, buf + (wave * WI + j) * 1024);
-      }
-    };
-    issue_w(0);
-    const uint8_t* asrc[AI];
-#pragma unroll
-    for (int j = 0; j < AI; ++j) {
-      const int m = (wave * AI + j) * kRowsPerAInst + lane / 32;
-      const uint16_t* rowp = GATEUP ? a.act + (size_t)(arow[j] / a.topk) * a.d
-                                    : a.act + (size_t)arow[j] * a.dff + kbeg;
-      asrc[j] = reinterpret_cast<const uint8_t*>(rowp) + 16 * achunk_pos(m, lane % 32);
-    }
-    // Activation rows past the tile's end are not copied (their LDS rows hold
-    // stale data, which only reaches output rows that are never stored).  An
-    // instruction whose rows all lie past the end is not issued at all: na of
-    // this wave's AI instructions are, the same number every stage.
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int na = min(AI, max(0, (rows - wave_u * AI * kRowsPerAInst + kRowsPerAInst - 1) / kRowsPerAInst));
-    auto issue_a = [&](int st) {
-      char* buf = smem + (st & 1) * SBYTES;
-      const bool half = half_last && st == nst - 1;
-#pragma unroll
-      for (int j = 0; j < AI; ++j) {
-        if (j < na) {
-          const int m = (wave * AI + j) * kRowsPerAInst + lane / 32;
-          if (m < rows && (!half || achunk_pos(m, lane % 32) < 16))
-            load_lds16(asrc[j] + (size_t)st * kARowBytes, buf + WBYTES + (wave * AI + j) * 1024);
-        }
-      }
-    };
-    issue_a(0);
-
-    f32x4 acc0[NCW], acc1[NCW], accs = {0, 0, 0, 0};
-#pragma unroll
-    for (int cb = 0; cb < NCW; ++cb) acc0[cb] = acc1[cb] = f32x4{0, 0, 0, 0};
-    const u32x4 ones = ones_bf16();
-
-    for (int st = 0; st < nst; ++st) {
-      if (st + 1 < nst) {
-        issue_w(st + 1);
-        issue_a(st + 1);
-      }
-      // wait for this stage's copies; the next stage's (WI + na instructions,
-      // unless it is a half stage, which counts as none: wait longer, never
-      // shorter) stay in flight
-      if (st + 1 < nst && !(half_last && st + 1 == nst - 1))
-        wait_vmem_rt<WI, AI>(WI + na);
-      else
-        wait_vmem<0>();
-      lds_barrier();
-      const char* buf = smem + (st & 1) * SBYTES;
-      const int nss = (half_last && st == nst - 1) ? 1 : 2;
-      for (int ss = 0; ss < nss; ++ss) {
-        const int c = 4 * ss + grp;
-        u32x4 b0[NCW], b1[NCW], av[4];
-#pragma unroll
-        for (int cb = 0; cb < NCW; ++cb) {
-          const int r0 = wave * 16 * NCW + cb * 16 + lr;
-          b0[cb] = lds_read16(buf + r0 * kWRowBytes + 16 * wchunk_pos(r0, c));
-          if (GATEUP) {
-            const int r1 = COLS + r0;
-            b1[cb] = lds_read16(buf + r1 * kWRowBytes + 16 * wchunk_pos(r1, c));
-          }
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) av[s] = lds_read16(buf + WBYTES + lr * kARowBytes + 16 * achunk_pos(lr, 16 * ss + 4 * grp + s));
-        lds_wait();
-#pragma unroll
-        for (int cb = 0; cb < NCW; ++cb) {
-          lds_ready(b0[cb]);
-          if (GATEUP) lds_ready(b1[cb]);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) lds_ready(av[s]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 x = GATEUP ? permute_a(av[s]) : av[s];  // h is stored in fragment order already
-#pragma unroll
-          for (int cb = 0; cb < NCW; ++cb) {
-            acc0[cb] = mfma16(x, codes_to_bf16(b0[cb][s]), acc0[cb]);
-            if (GATEUP) acc1[cb] = mfma16(x, codes_to_bf16(b1[cb][s]), acc1[cb]);
-          }
-          accs = mfma16(x, ones, accs);
-        }
-      }
-      lds_barrier();
-    }
-
-#pragma unroll
-    for (int cb = 0; cb < NCW; ++cb) {
-      const int n = n0 + wave * 16 * NCW + cb * 16 + lr;
-      const size_t sidx = (size_t)slot * ncols_total + n;
-      const float sc0 = fp16_to_f32(a.s0[sidx]), cc0 = kCodeBias + fp16_to_f32(a.z0[sidx]);
-      float sc1 = 0.0f, cc1 = 0.0f;
-      if (GATEUP) {
-        sc1 = fp16_to_f32(a.s1[sidx]);
-        cc1 = kCodeBias + fp16_to_f32(a.z1[sidx]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = grp * 4 + i;
-        if (row < rows) {
-          const float sx = accs[i];
-          const float v0 = sc0 * (acc0[cb][i] - cc0 * sx);
-          if (GATEUP) {
-            const float v1 = sc1 * (acc1[cb][i] - cc1 * sx);
-            a.h[(size_t)(pbase + row) * a.dff + h_phys_col(n)] = f32_to_bf16(silu(v0) * v1);
-          } else {
-            store_coherent(&yrow[(size_t)row * a.d + n], v0);
-          }
-        }
-      }
-    }
-  }
-
-  if (GATEUP || a.fc.tickets == nullptr) return;
-  // fused combine: the last block of this column slice gathers it for every token
-  if (!last_block_ticket(&a.fc.tickets[blockIdx.x], (uint32_t)(ntiles * gridDim.z), &is_last)) return;
+  if (!last_block_ticket(&a.fc.tickets[bx], (uint32_t)(ntiles * gridDim.z), &is_last)) return;
   const int nsplit = gridDim.z;
+  const int n0 = bx * COLS;
   __shared__ int rp[kStreamMaxTokens * 8];
   __shared__ float rw[kStreamMaxTokens * 8];
   for (int i = threadIdx.x; i < a.fc.T * a.fc.k; i += 256) {
@@ -322,15 +150,236 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
     }
     a.fc.out[(size_t)t * a.d + col] = f32_to_bf16(acc);
   }
-  if (threadIdx.x == 0) reset_ticket(&a.fc.tickets[blockIdx.x]);
+  if (threadIdx.x == 0) reset_ticket(&a.fc.tickets[bx]);
+}
+
+// GATEUP: h rows of one tile, silu(x Wg^T) * (x Wu^T) in bf16, columns of
+// every group of 8 in the fragment k-order (h_phys_col).
+// !GATEUP: ypart[split][p] = h[p] Wd^T over the k range of `split`, fp32,
+// written with coherent stores; with a FusedCombine, the last block of each
+// column slice also writes that slice of out[].
+#ifndef MOE_STREAM_WPE
+#define MOE_STREAM_WPE 4
+#endif
+template <bool GATEUP, int NCW, int NBUF, int KW, bool NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_STREAM_WPE)))
+void stream_gemm_kernel(StreamArgs a) {
+  static_assert(NBUF == 2 || NBUF == 3, "stage ring of 2 or 3 buffers");
+  static_assert(KW == 2 || KW == 4, "k split over 2 or 4 waves");
+  constexpr int COLS = 64 * NCW;                        // output columns per block
+  constexpr int NWR = (GATEUP ? 2 : 1) * COLS;          // weight rows per stage
+  constexpr int WBYTES = NWR * kWRowBytes;              // one stage buffer
+  constexpr int WI = NWR / kRowsPerWInst / 4;           // weight-load instructions per wave per stage
+  constexpr int CW = 4 / KW;                            // column parts
+  constexpr int CT = COLS / 16 / CW;                    // 16-column tiles per wave and weight matrix
+  constexpr int NB = (GATEUP ? 2 : 1) * CT;             // B fragments per wave per stage
+  constexpr int KR = kStageK / KW;                      // k per wave per stage
+  constexpr int KS = KR / 32;                           // MFMA k-steps per wave per stage (16 B of A each)
+  static_assert(WI * kRowsPerWInst * 4 == NWR, "even split over waves");
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * WBYTES];
+
+  const int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;  // column slice, row tile, k-split
+  const int ntiles = *a.num_tiles;
+  const int tile = by;
+  if (tile >= ntiles) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, grp = lane >> 4;
+  const int kp = wave % KW, cp = wave / KW;
+  const int n0 = bx * COLS;
+  const int4 td = a.tiles[tile];  // (expert, slot, first grouped row, rows <= 16)
+  const int slot = td.y, pbase = td.z, rows = td.w;
+  const int ncols_total = GATEUP ? a.dff : a.d;
+  const int K = GATEUP ? a.d : a.kchunk;
+  const int kbeg = GATEUP ? 0 : bz * a.kchunk;
+  const size_t row_bytes = (size_t)(GATEUP ? a.d : a.dff) / 2;
+  const bool bad = slot < 0 || slot >= a.num_slots;
+  float* yrow = GATEUP ? nullptr : a.ypart + ((size_t)bz * a.R + pbase) * a.d;
+
+  if (bad) {
+    if (threadIdx.x == 0) atomicOr(a.flags, MOE_FLAG_BAD_SLOT);
+    if (GATEUP) return;
+    for (int i = threadIdx.x; i < rows * COLS; i += 256) store_coherent(&yrow[(size_t)(i / COLS) * a.d + n0 + i % COLS], 0.0f);
+  } else {
+    // this lane's activation row (row lr of the tile) and k offset in every
+    // stage: KR kp + (KR / 4) grp, KS x 8 values
+    const int mm = lr < rows ? lr : 0;
+    const int ka = KR * kp + (KR / 4) * grp;
+    const uint16_t* asrc = GATEUP ? a.act + (size_t)(a.perm[pbase + mm] / a.topk) * a.d + ka
+                                  : a.act + (size_t)(pbase + mm) * a.dff + kbeg + ka;
+    const uint8_t* wsrc[WI];
+#pragma unroll
+    for (int j = 0; j < WI; ++j) {
+      const int r = (wave * WI + j) * kRowsPerWInst + lane / 8;  // block weight row
+      const uint8_t* base = (!GATEUP || r < COLS) ? a.w0 : a.w1;
+      const int n = n0 + (r % COLS);
+      wsrc[j] = base + ((size_t)slot * ncols_total + n) * row_bytes + kbeg / 2 + 16 * wchunk_pos(r, lane % 8);
+    }
+    const int nst = (K + kStageK - 1) / kStageK;
+    const bool half_last = (K % kStageK) != 0;  // the last stage has only its lower 128 k
+    const bool idle_half = KR * kp >= kStageK / 2;  // this wave has no k in a half stage
+    // The copies are issued without per-lane conditions, so that the
+    // compiler's own wait for the activation registers is exact: a half
+    // stage copies its upper 4 chunks from the lower ones (into LDS nobody
+    // reads), and lanes of rows past the tile's end load row 0 (their
+    // registers only reach output rows that are never stored).
+    auto issue_w = [&](int st) {
+      char* buf = smem + (st % NBUF) * WBYTES;
+      const bool half = half_last && st == nst - 1;
+#pragma unroll
+      for (int j = 0; j < WI; ++j) {
+        const int r = (wave * WI + j) * kRowsPerWInst + lane / 8;
+        const int back = (half && wchunk_pos(r, lane % 8) >= 4) ? 64 : 0;
+        load_lds16<NT>(wsrc[j] + (size_t)st * kWRowBytes - back, buf + (wave * WI + j) * 1024);
+      }
+    };
+    auto load_a = [&](int st, u32x4* av) {
+      const int sa = (half_last && st == nst - 1 && idle_half) ? 0 : st;
+      const u32x4* src = reinterpret_cast<const u32x4*>(asrc + (size_t)sa * kStageK);
+#pragma unroll
+      for (int j = 0; j < KS; ++j) av[j] = src[j];
+    };
+
+    f32x4 acc[NB], accs = {0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < NB; ++t) acc[t] = f32x4{0, 0, 0, 0};
+    const u32x4 ones = ones_bf16();
+    // this lane's bytes of every weight row: (KR / 8) bytes at KR / 2 kp + (KR / 8) grp
+    const int boff = (KR / 2) * kp + (KR / 8) * grp;
+    auto compute = [&](int st, const u32x4* acur) {
+      if (half_last && st == nst - 1 && idle_half) return;
+      const char* buf = smem + (st % NBUF) * WBYTES;
+      uint32_t bw[NB][KS];
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        const int r = (t >= CT ? COLS : 0) + 16 * (CT * cp + t % CT) + lr;
+        const char* p = buf + r * kWRowBytes + 16 * wchunk_pos(r, boff / 16) + boff % 16;
+        if constexpr (KS == 4) {
+          const u32x4 v = lds_read16(p);
+          bw[t][0] = v.x; bw[t][1] = v.y; bw[t][2] = v.z; bw[t][3] = v.w;
+        } else {
+          const u32x2 v = lds_read8(p);
+          bw[t][0] = v.x; bw[t][1] = v.y;
+        }
+      }
+      lds_wait();
+#pragma unroll
+      for (int t = 0; t < NB; ++t)
+#pragma unroll
+        for (int j = 0; j < KS; ++j) lds_ready(bw[t][j]);
+      u32x4 x[KS];
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        x[j] = GATEUP ? permute_a(acur[j]) : acur[j];  // h is stored in fragment order already
+        accs = mfma16(x[j], ones, accs);
+      }
+#pragma unroll
+      for (int t = 0; t < NB; ++t)
+#pragma unroll
+        for (int j = 0; j < KS; ++j) acc[t] = mfma16(x[j], codes_to_bf16(bw[t][j]), acc[t]);
+    };
+
+    // Issue order: A(0), W(0) .. W(NBUF - 2); then at stage s, A(s + 1) and
+    // W(s + NBUF - 1).  At stage s the copies younger than W(s) are at least
+    // A(s + 1) and W(s + 1) (NBUF = 2), or W(s + 1), A(s + 1) and W(s + 2)
+    // (NBUF = 3), so waiting until that many are pending completes W(s).
+    // The last NBUF - 1 stages issue no weight copies and wait for all.
+    constexpr int kPending = (NBUF - 1) * WI + KS;
+    u32x4 anx[KS], acur[KS];
+    load_a(0, anx);
+    issue_w(0);
+    if (NBUF == 3 && nst > 1) issue_w(1);
+    const int nmain = max(0, nst - (NBUF - 1));
+    for (int st = 0; st < nmain; ++st) {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) acur[j] = anx[j];
+      load_a(st + 1, anx);
+      issue_w(st + NBUF - 1);
+      wait_vmem<kPending>();
+      lds_barrier();
+      compute(st, acur);
+      lds_barrier();
+    }
+    // scale and code offset (128 + z) of this wave's columns, loaded while the last stages land
+    const size_t sbase = (size_t)slot * ncols_total + n0;
+    float sc[NB], cc[NB];
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const int nl = 16 * (CT * cp + t % CT) + lr;  // column inside the block
+      const bool up = GATEUP && t >= CT;
+      sc[t] = fp16_to_f32((up ? a.s1 : a.s0)[sbase + nl]);
+      cc[t] = kCodeBias + fp16_to_f32((up ? a.z1 : a.z0)[sbase + nl]);
+    }
+    for (int st = nmain; st < nst; ++st) {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) acur[j] = anx[j];
+      if (st + 1 < nst) load_a(st + 1, anx);
+      wait_vmem<0>();
+      lds_barrier();
+      compute(st, acur);
+      lds_barrier();
+    }
+
+    // Every wave turns its k part into s (acc - (128 + z) sum_k a) -- linear
+    // in the k parts -- and hands it over through LDS (the ring is free);
+    // the KW waves of a column part then add the k parts in fixed order, each
+    // for the column tiles it owns (local tile tl with tl % KW == kp).
+    float* part = reinterpret_cast<float*>(smem);  // [wave][tile][4][64]
+    static_assert(4 * NB * 4 * 64 * 4 <= NBUF * WBYTES, "the k-part hand-over fits the stage ring");
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[((wave * NB + t) * 4 + i) * 64 + lane] = sc[t] * (acc[t][i] - cc[t] * accs[i]);
+    __syncthreads();
+    uint16_t* hrow = GATEUP ? a.h + (size_t)pbase * a.dff + n0 : nullptr;
+    float* ybase = GATEUP ? nullptr : yrow + n0;
+    for (int tl = kp; tl < CT; tl += KW) {
+      const int nl = 16 * (CT * cp + tl) + lr;
+      float v0[4] = {0, 0, 0, 0}, v1[4] = {0, 0, 0, 0};
+      for (int q = 0; q < KW; ++q) {
+        const int wq = cp * KW + q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v0[i] += part[((wq * NB + tl) * 4 + i) * 64 + lane];
+          if (GATEUP) v1[i] += part[((wq * NB + CT + tl) * 4 + i) * 64 + lane];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = grp * 4 + i;
+        if (row < rows) {
+          if (GATEUP)
+            hrow[(uint32_t)(row * a.dff + h_phys_col(nl))] = f32_to_bf16(silu(v0[i]) * v1[i]);
+          else
+            store_coherent(&ybase[(uint32_t)(row * a.d + nl)], v0[i]);
+        }
+      }
+    }
+  }
+
+  if (GATEUP || a.fc.tickets == nullptr) return;
+  fused_combine_tail<COLS>(a, bx, ntiles);
 }
 
 namespace {
+#ifndef MOE_STREAM_NBUF
+#define MOE_STREAM_NBUF 2
+#endif
+#ifndef MOE_STREAM_KW_GU
+#define MOE_STREAM_KW_GU 4
+#endif
+#ifndef MOE_STREAM_KW_DN
+#define MOE_STREAM_KW_DN 4
+#endif
+// Weights are streamed with the nt hint: most lines are read once per launch,
+// and early eviction keeps the activations and the router's inputs (read
+// again by the next layer step) in the caches.  Measured to help every
+// decode shape, multi-tile experts included.
 template <bool GATEUP, int NCW>
 void launch_stream(const moe_config& c, const Plan& p, const StreamArgs& args, hipStream_t s) {
   const int ncols = GATEUP ? c.d_ff : c.d_model;
   dim3 grid(ncols / (64 * NCW), p.max_tiles, GATEUP ? 1 : p.down_split);
-  stream_gemm_kernel<GATEUP, NCW><<<grid, 256, 0, s>>>(args);
+  constexpr int KW = GATEUP ? MOE_STREAM_KW_GU : MOE_STREAM_KW_DN;
+  stream_gemm_kernel<GATEUP, NCW, MOE_STREAM_NBUF, KW, true><<<grid, 256, 0, s>>>(args);
 }
 }  // namespace
 
