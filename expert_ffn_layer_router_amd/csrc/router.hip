@@ -149,18 +149,19 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
   if (!last_block_ticket(ticket, gridDim.x * gridDim.y, &is_last)) return;
   if (threadIdx.x == 0) *flags = 0u;
   if (T * E <= kFusedLogitsLds && T <= 256) {
-    // slot table and the biased logits, rounded to fp32, into LDS (transposed:
-    // lgf[e * T + t]) in one round of loads; the fp64 values stay in global memory
+    // slot table and the biased logits into LDS, in fp64 and rounded to fp32
+    // (transposed: lg[e * T + t]), in one round of loads
+    __shared__ double lgd[kFusedLogitsLds];
     __shared__ float lgf[kFusedLogitsLds];
     __shared__ int32_t sslot[256];
-    __shared__ double sbias[256];
     __shared__ int32_t sid[256 * 8];
-    for (int e = threadIdx.x; e < E; e += 256) {
-      sslot[e] = ra.slot_table[e];
-      sbias[e] = bias ? (double)bias[e] : 0.0;
+    for (int e = threadIdx.x; e < E; e += 256) sslot[e] = ra.slot_table[e];
+    for (int i = threadIdx.x; i < T * E; i += 256) {
+      const int t = i / E, e = i % E;
+      const double v = load_coherent(&logits[i]) + (bias ? (double)bias[e] : 0.0);
+      lgd[e * T + t] = v;
+      lgf[e * T + t] = (float)v;
     }
-    __syncthreads();  // sbias ready
-    for (int i = threadIdx.x; i < T * E; i += 256) lgf[(i % E) * T + i / E] = (float)(load_coherent(&logits[i]) + sbias[i % E]);
     __syncthreads();
     // rank of every (token, expert): the experts that beat it -- a larger
     // logit, or an equal logit and a lower id.  Rank r < k is choice r.  The
@@ -188,10 +189,10 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
         tie |= (int)(f2 == f) & (int)(e2 != e);
       }
       if (tie) {  // rare: count again in fp64
-        const double l = load_coherent(&logits[(size_t)t * E + e]) + sbias[e];
+        const double l = lgd[i];
         r = 0;
         for (int e3 = 0; e3 < E; ++e3) {
-          const double l2 = load_coherent(&logits[(size_t)t * E + e3]) + sbias[e3];
+          const double l2 = lgd[e3 * T + t];
           r += (int)(l2 > l) | ((int)(l2 == l) & (int)(e3 < e));
         }
       }
@@ -201,10 +202,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
     if (threadIdx.x < T) {
       const int t = threadIdx.x;
       double lc[8];  // the chosen biased logits, fp64
-      for (int j = 0; j < k; ++j) {
-        const int e = sid[t * k + j];
-        lc[j] = load_coherent(&logits[(size_t)t * E + e]) + sbias[e];
-      }
+      for (int j = 0; j < k; ++j) lc[j] = lgd[sid[t * k + j] * T + t];
       float ex[8], den = 0.0f;
       for (int j = 0; j < k; ++j) {
         ex[j] = expf((float)(lc[j] - lc[0]));
