@@ -150,17 +150,40 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
   if (threadIdx.x == 0) *flags = 0u;
   if (T * E <= kFusedLogitsLds && T <= 256) {
     // slot table and the biased logits into LDS, in fp64 and rounded to fp32
-    // (transposed: lg[e * T + t]), in one round of loads
-    __shared__ double lgd[kFusedLogitsLds];
-    __shared__ float lgf[kFusedLogitsLds];
+    // (transposed: lg[e * T + t]).  The coherent loads see the latency of the
+    // memory side of the L2, so they are issued without conditions, four per
+    // thread in flight at a time (indices past the end re-read the last logit
+    // and land in a spare LDS slot), together with the bias and slot loads.
+    __shared__ double lgd[kFusedLogitsLds + 1];
+    __shared__ float lgf[kFusedLogitsLds + 1];
+    __shared__ double sbias[256];
     __shared__ int32_t sslot[256];
     __shared__ int32_t sid[256 * 8];
-    for (int e = threadIdx.x; e < E; e += 256) sslot[e] = ra.slot_table[e];
-    for (int i = threadIdx.x; i < T * E; i += 256) {
-      const int t = i / E, e = i % E;
-      const double v = load_coherent(&logits[i]) + (bias ? (double)bias[e] : 0.0);
-      lgd[e * T + t] = v;
-      lgf[e * T + t] = (float)v;
+    const int TE = T * E;
+    for (int i0 = 0; i0 < TE; i0 += 4 * 256) {
+      float bv = 0.0f;
+      int sl = 0;
+      if (i0 == 0 && threadIdx.x < E) {
+        bv = bias ? bias[threadIdx.x] : 0.0f;
+        sl = ra.slot_table[threadIdx.x];
+      }
+      double v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = load_coherent(&logits[min(i0 + (int)threadIdx.x + 256 * u, TE - 1)]);
+      if (i0 == 0 && threadIdx.x < E) {
+        sbias[threadIdx.x] = bv;
+        sslot[threadIdx.x] = sl;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + (int)threadIdx.x + 256 * u;
+        const int t = i / E, e = i % E;
+        const int dst = i < TE ? e * T + t : kFusedLogitsLds;
+        const double b = v[u] + sbias[i < TE ? e : 0];
+        lgd[dst] = b;
+        lgf[dst] = (float)b;
+      }
     }
     __syncthreads();
     // rank of every (token, expert): the experts that beat it -- a larger
