@@ -93,6 +93,8 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   p->fused_small = T <= kStreamMaxTokens;
   if (T <= kStreamMaxTokens) {
     p->router_split = 0;
+    // one 512-k pass per wave: k-split in multiples of 128, up to kRouterSmallMaxSplit
+    p->small_split = largest_divisor_at_most(c.d_model / 128, std::max(1, std::min(kRouterSmallMaxSplit, c.d_model / 2048)));
   } else {
     // 64-token x router_tile_experts(E) tiles; split k (in multiples of 32) until about 512 blocks
     const int tiles = ((T + kRouterMfmaTokens - 1) / kRouterMfmaTokens) *
@@ -122,7 +124,7 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   p->ctrl = take(4 * (1 + (size_t)c.d_model / kStreamCols));
   p->ctrl_bytes = off;  // aligned end of the control words (they start at offset 0)
   p->flags = take(4);
-  p->logits = take(sizeof(double) * (size_t)std::max(1, p->router_split) * T * E);
+  p->logits = take(sizeof(double) * (size_t)std::max({1, p->router_split, p->small_split}) * T * E);
   p->topk_idx = take(4 * R);
   p->topk_w = take(4 * R);
   p->counts = take(4 * (size_t)E);

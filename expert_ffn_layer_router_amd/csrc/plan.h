@@ -12,6 +12,7 @@
 namespace moe {
 
 constexpr int kRouterTokTile = 16;     // tokens per router wave
+constexpr int kRouterSmallMaxSplit = 4;  // few-token router: at most this many k-splits
 constexpr int kRouterMfmaTokens = 64;  // many-token router: tokens per block tile (16 per wave)
 constexpr int kRouterMfmaK = 32;       // many-token router: k per LDS chunk
 // many-token router: experts per block tile (a multiple of 16, the MFMA width)
@@ -42,6 +43,7 @@ struct Plan {
   int T = 0, R = 0;
   GemmFamily family = GemmFamily::kPrefill;
   int router_split = 0;       // 0: few-token router; else k-splits of the tiled router
+  int small_split = 1;        // few-token router: k-splits (blocks per expert and token group)
   int gateup_ncw = 1, down_ncw = 1;  // decode family: blocks of 64 x ncw output columns
   int tile_rows = kPrefillTileRows;  // rows of an expert group per GEMM row tile
   int down_split = 1;         // k-split of the down projection

@@ -36,6 +36,7 @@ __device__ void topk_token(const double* __restrict__ logits, int nsplit, const 
     if (live[j]) {
       if (kCoherent) {
         v = load_coherent(&logits[(size_t)t * E + e]);
+        for (int s = 1; s < nsplit; ++s) v += load_coherent(&logits[((size_t)s * T + t) * E + e]);
       } else {
         v = logits[(size_t)t * E + e];
         for (int s = 1; s < nsplit; ++s) v += logits[((size_t)s * T + t) * E + e];
@@ -110,10 +111,11 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
   double acc[kRouterTokTile];
 #pragma unroll
   for (int t = 0; t < kRouterTokTile; ++t) acc[t] = 0.0;
-  const int kq = d / 4;
-  const int kend = (wave + 1) * kq;
+  const int nsplit = gridDim.z;          // k-splits: block z covers k in [z d / nsplit, (z + 1) d / nsplit)
+  const int kq = d / (4 * nsplit);       // per wave, a multiple of 32
+  const int kbeg = blockIdx.z * (d / nsplit) + wave * kq, kend = kbeg + kq;
   const float* wrow = wr + (size_t)e * d;
-  for (int kk = wave * kq + lane * 8; kk < kend; kk += 512) {
+  for (int kk = kbeg + lane * 8; kk < kend; kk += 512) {
     const float4 w0 = *reinterpret_cast<const float4*>(wrow + kk);
     const float4 w1 = *reinterpret_cast<const float4*>(wrow + kk + 4);
     const double wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -143,19 +145,18 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
   __syncthreads();
   if (wave == 0 && lane < nt) {
     const double v = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
-    store_coherent(&logits[(size_t)(t0 + lane) * E + e], v);
+    store_coherent(&logits[((size_t)blockIdx.z * T + t0 + lane) * E + e], v);
   }
   // the last block to finish does the top-k of every token and the regroup
-  if (!last_block_ticket(ticket, gridDim.x * gridDim.y, &is_last)) return;
+  if (!last_block_ticket(ticket, gridDim.x * gridDim.y * gridDim.z, &is_last)) return;
   if (threadIdx.x == 0) *flags = 0u;
   if (T * E <= kFusedLogitsLds && T <= 256) {
-    // slot table and the biased logits into LDS, in fp64 and rounded to fp32
-    // (transposed: lg[e * T + t]).  The coherent loads see the latency of the
-    // memory side of the L2, so they are issued without conditions, four per
-    // thread in flight at a time (indices past the end re-read the last logit
-    // and land in a spare LDS slot), together with the bias and slot loads.
-    __shared__ double lgd[kFusedLogitsLds + 1];
-    __shared__ float lgf[kFusedLogitsLds + 1];
+    // slot table and the biased fp64 logits into LDS (lg[t * E + e]).  The
+    // coherent loads see the latency of the memory side of the L2, so they
+    // are issued without conditions, four per thread in flight at a time
+    // (indices past the end re-read the last logit and land in a spare LDS
+    // slot), together with the bias and slot loads.
+    __shared__ double lg[kFusedLogitsLds + 1];
     __shared__ double sbias[256];
     __shared__ int32_t sslot[256];
     __shared__ int32_t sid[256 * 8];
@@ -167,9 +168,21 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
         bv = bias ? bias[threadIdx.x] : 0.0f;
         sl = ra.slot_table[threadIdx.x];
       }
-      double v[4];
+      // logit = split 0 + split 1 + ... in order; up to kRouterSmallMaxSplit
+      // splits are loaded (missing ones re-read split 0 and add zero)
+      double v[4], w[4][kRouterSmallMaxSplit - 1];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = load_coherent(&logits[min(i0 + (int)threadIdx.x + 256 * u, TE - 1)]);
+      for (int u = 0; u < 4; ++u) {
+        const int i = min(i0 + (int)threadIdx.x + 256 * u, TE - 1);
+        v[u] = load_coherent(&logits[i]);
+#pragma unroll
+        for (int sp = 1; sp < kRouterSmallMaxSplit; ++sp)
+          w[u][sp - 1] = load_coherent(&logits[(size_t)(sp < nsplit ? sp : 0) * TE + i]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int sp = 1; sp < kRouterSmallMaxSplit; ++sp) v[u] += sp < nsplit ? w[u][sp - 1] : 0.0;
       if (i0 == 0 && threadIdx.x < E) {
         sbias[threadIdx.x] = bv;
         sslot[threadIdx.x] = sl;
@@ -178,62 +191,66 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = i0 + (int)threadIdx.x + 256 * u;
-        const int t = i / E, e = i % E;
-        const int dst = i < TE ? e * T + t : kFusedLogitsLds;
-        const double b = v[u] + sbias[i < TE ? e : 0];
-        lgd[dst] = b;
-        lgf[dst] = (float)b;
+        lg[i < TE ? i : kFusedLogitsLds] = v[u] + sbias[i < TE ? i % E : 0];
       }
     }
     __syncthreads();
-    // rank of every (token, expert): the experts that beat it -- a larger
-    // logit, or an equal logit and a lower id.  Rank r < k is choice r.  The
-    // counting runs on the fp32 copies, without branches and with 8 LDS reads
-    // in flight: rounding is monotonic, so a strictly larger (smaller) fp32
-    // value means a strictly larger (smaller) fp64 one; a pair whose fp32
-    // values tie is counted again exactly in fp64.
-    for (int i = threadIdx.x; i < T * E; i += 256) {
-      const int t = i % T, e = i / T;
-      const float f = lgf[i];
-      int r = 0, tie = 0, e2 = 0;
-      for (; e2 + 8 <= E; e2 += 8) {
-        float f2[8];
+    // Top-k of every token at once: a segment of S lanes per token (S a power
+    // of two, S * T <= 256), lane j of the segment holding experts j, j + S,
+    // ...  Each of the k rounds takes every lane's best live expert (largest
+    // fp64 logit, lowest id), reduces the segment with a butterfly, and
+    // retires the winner; w_j = exp(l_j - l_0) / sum exp(l_i - l_0).
+    int S = 64;
+    while (S > 1 && S * T > 256) S >>= 1;
+    const int seg = threadIdx.x / S, j = threadIdx.x % S;
+    const int t = seg;
+    if (t < T) {
+      const double* lt = lg + (size_t)t * E;
+      uint64_t dead = 0;  // bit m: expert j + S m chosen (E / S <= 64)
+      double val[8];
+      int cid[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) f2[u] = lgf[(e2 + u) * T + t];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          r += (int)(f2[u] > f);
-          tie |= (int)(f2[u] == f) & (int)(e2 + u != e);
+      for (int r = 0; r < 8; ++r) {
+        val[r] = 0.0;
+        cid[r] = 0;
+        if (r < k) {
+          double best = 0.0;
+          int bid = 0x7fffffff;
+          for (int e = j, m = 0; e < E; e += S, ++m) {
+            const double v = lt[e];
+            if (!((dead >> m) & 1) && (bid == 0x7fffffff || v > best)) {
+              best = v;
+              bid = e;
+            }
+          }
+          for (int off = S >> 1; off >= 1; off >>= 1) {
+            const double ov = __shfl_xor(best, off, 64);
+            const int oid = __shfl_xor(bid, off, 64);
+            if (oid != 0x7fffffff && (bid == 0x7fffffff || ov > best || (ov == best && oid < bid))) {
+              best = ov;
+              bid = oid;
+            }
+          }
+          val[r] = best;
+          cid[r] = bid;
+          if (bid % S == j) dead |= 1ull << (bid / S);
         }
       }
-      for (; e2 < E; ++e2) {
-        const float f2 = lgf[e2 * T + t];
-        r += (int)(f2 > f);
-        tie |= (int)(f2 == f) & (int)(e2 != e);
-      }
-      if (tie) {  // rare: count again in fp64
-        const double l = lgd[i];
-        r = 0;
-        for (int e3 = 0; e3 < E; ++e3) {
-          const double l2 = lgd[e3 * T + t];
-          r += (int)(l2 > l) | ((int)(l2 == l) & (int)(e3 < e));
+      if (j == 0) {
+        float ex[8], den = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          ex[r] = r < k ? expf((float)(val[r] - val[0])) : 0.0f;
+          den += ex[r];
         }
-      }
-      if (r < k) sid[t * k + r] = e;
-    }
-    __syncthreads();
-    if (threadIdx.x < T) {
-      const int t = threadIdx.x;
-      double lc[8];  // the chosen biased logits, fp64
-      for (int j = 0; j < k; ++j) lc[j] = lgd[sid[t * k + j] * T + t];
-      float ex[8], den = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        ex[j] = expf((float)(lc[j] - lc[0]));
-        den += ex[j];
-      }
-      for (int j = 0; j < k; ++j) {
-        topk_idx[(size_t)t * k + j] = sid[t * k + j];
-        topk_w[(size_t)t * k + j] = ex[j] / den;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          if (r < k) {
+            topk_idx[(size_t)t * k + r] = cid[r];
+            topk_w[(size_t)t * k + r] = ex[r] / den;
+            sid[t * k + r] = cid[r];
+          }
+        }
       }
     }
     __syncthreads();
@@ -244,7 +261,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
     if (threadIdx.x == 0) reset_ticket(ticket);
     return;
   }
-  for (int t = wave; t < T; t += 4) topk_token<true>(logits, 1, bias, T, E, k, t, lane, topk_idx, topk_w);
+  for (int t = wave; t < T; t += 4) topk_token<true>(logits, nsplit, bias, T, E, k, t, lane, topk_idx, topk_w);
   __syncthreads();
   regroup_block<256>(ra);
   if (threadIdx.x == 0) reset_ticket(ticket);
@@ -364,7 +381,7 @@ void launch_router(const moe_config& c, const Plan& p, const uint16_t* hidden, c
   float* topk_w = reinterpret_cast<float*>(ws + p.topk_w);
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws + p.flags);
   if (p.fused_small) {
-    dim3 grid(c.num_experts, (p.T + kRouterTokTile - 1) / kRouterTokTile);
+    dim3 grid(c.num_experts, (p.T + kRouterTokTile - 1) / kRouterTokTile, p.small_split);
     router_small_kernel<<<grid, 256, 0, s>>>(hidden, router_w, router_bias, logits, p.T, c.d_model,
                                              c.num_experts, c.top_k, topk_idx, topk_w, flags,
                                              reinterpret_cast<uint32_t*>(ws + p.ctrl),

@@ -88,7 +88,7 @@ def test_zero_router_ties_go_to_lowest_ids():
     assert_out_close(res["out"], ref["out"])
 
 
-@pytest.mark.parametrize("E,k", [(1, 1), (4, 4), (8, 1), (16, 8)])
+@pytest.mark.parametrize("E,k", [(1, 1), (4, 4), (8, 1), (16, 8), (256, 8)])
 def test_small_special_shapes(E, k):
     require_gpu()
     shape = synth.LayerShape(24, 128, 256, E, k, E, "identity", 0.0)
