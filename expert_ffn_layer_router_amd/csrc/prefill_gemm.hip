@@ -20,6 +20,8 @@
 // are applied in the epilogue with precomputed row sums of A (token row sums
 // from the router, h row sums from the gate/up epilogue), which keeps the
 // matrix cores free of the extra row-sum product the decode kernels use.
+#include <type_traits>
+
 #include "device_common.h"
 #include "plan.h"
 
@@ -59,6 +61,12 @@ constexpr int kPrefillDownStages = MOE_PF_DN_STAGES, kPrefillDownBlocks = MOE_PF
 #endif
 #ifndef MOE_PF_DN_NW
 #define MOE_PF_DN_NW 4
+#endif
+#ifndef MOE_PF_DN_NJ
+#define MOE_PF_DN_NJ 4
+#endif
+#ifndef MOE_PF_DN_WN
+#define MOE_PF_DN_WN MOE_PF_DN_NW
 #endif
 // gate/up blocks: 64 NJ weight rows (32 NJ output columns) on NW waves, 1 x NW;
 // down blocks: 256 weight rows on NW waves, 1 x NW
@@ -221,54 +229,74 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
   for (int j = 0; j < NJW; ++j)
     wr[j] = GATEUP ? (j < HJ ? 32 * HJ * wn + 32 * j : kWRows / 2 + 32 * HJ * wn + 32 * (j - HJ)) : 32 * NJW * wn + 32 * j;
 
+  // row blocks of 32 of this wave that hold rows of the tile (the rest are
+  // skipped: a tile's last rows may be missing)
+  const int live_mi = __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows - 32 * MI * wm + 31) / 32)));
   const int nst = K / kBK;
 #pragma unroll
   for (int st = 0; st < kNBuf - 1; ++st)
     if (st < nst) issue(st);
-  for (int st = 0; st < nst; ++st) {
-    // wait until stage st has landed (the later stages issued so far -- at
-    // most kNBuf - 2 -- may stay in flight), then a barrier: every wave is
-    // past stage st - 1, so its buffer can be refilled with stage st + kNBuf - 1
-    const int later = min(kNBuf - 2, nst - 1 - st);
-    if (kNBuf > 3 && later >= 2)
-      wait_vmem<(kNBuf > 3 ? 2 : 0) * (kAI + kWI)>();
-    else if (kNBuf > 2 && later >= 1)
-      wait_vmem<(kNBuf > 2 ? 1 : 0) * (kAI + kWI)>();
-    else
-      wait_vmem<0>();
-    lds_barrier();
-    if (st + kNBuf - 1 < nst) issue(st + kNBuf - 1);
-    const char* buf = smem + (st % kNBuf) * kStage;
-    u32x4 bq[NJW];
-#pragma unroll
-    for (int j = 0; j < NJW; ++j) {
-      const int r = wr[j] + l32;
-      bq[j] = *reinterpret_cast<const u32x4*>(buf + kABytes + r * kWRow + 16 * wpos(r, hh));
-    }
-    // A fragments (fragment order already) of step s; the next step's are read
-    // before this step's products, so the LDS latency hides behind them
-    auto read_a = [&](int s, u32x4(&av)[MI]) {
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int r = 32 * MI * wm + 32 * i + l32;
-        av[i] = *reinterpret_cast<const u32x4*>(buf + r * kARow + 16 * apos(r, 4 * hh + s));
-      }
-    };
-    u32x4 av0[MI], av1[MI];
-    read_a(0, av0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4(&cur)[MI] = (s & 1) ? av1 : av0;
-      u32x4(&nxt)[MI] = (s & 1) ? av0 : av1;
-      if (s + 1 < 4) read_a(s + 1, nxt);
+  // The main loop for ML live row blocks of 32 (a tile's last rows may be
+  // missing; their products are skipped), instantiated for each ML so that
+  // the loop carries no branches.
+  auto main_loop = [&](auto ml_tag) {
+    constexpr int ML = decltype(ml_tag)::value;
+    for (int st = 0; st < nst; ++st) {
+      // wait until stage st has landed (the later stages issued so far -- at
+      // most kNBuf - 2 -- may stay in flight), then a barrier: every wave is
+      // past stage st - 1, so its buffer can be refilled with stage st + kNBuf - 1
+      const int later = min(kNBuf - 2, nst - 1 - st);
+      if (kNBuf > 3 && later >= 2)
+        wait_vmem<(kNBuf > 3 ? 2 : 0) * (kAI + kWI)>();
+      else if (kNBuf > 2 && later >= 1)
+        wait_vmem<(kNBuf > 2 ? 1 : 0) * (kAI + kWI)>();
+      else
+        wait_vmem<0>();
+      lds_barrier();
+      if (st + kNBuf - 1 < nst) issue(st + kNBuf - 1);
+      const char* buf = smem + (st % kNBuf) * kStage;
+      u32x4 bq[NJW];
 #pragma unroll
       for (int j = 0; j < NJW; ++j) {
-        const u32x4 b = codes_to_bf16(bq[j][s]);
+        const int r = wr[j] + l32;
+        bq[j] = *reinterpret_cast<const u32x4*>(buf + kABytes + r * kWRow + 16 * wpos(r, hh));
+      }
+      // A fragments (fragment order already) of step s; the next step's are read
+      // before this step's products, so the LDS latency hides behind them
+      auto read_a = [&](int s, u32x4(&av)[MI]) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) acc[i][j] = mfma32(cur[i], b, acc[i][j]);
+        for (int i = 0; i < MI; ++i) {
+          const int r = 32 * MI * wm + 32 * i + l32;
+          if (i < ML) av[i] = *reinterpret_cast<const u32x4*>(buf + r * kARow + 16 * apos(r, 4 * hh + s));
+        }
+      };
+      u32x4 av0[MI], av1[MI];
+      read_a(0, av0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4(&cur)[MI] = (s & 1) ? av1 : av0;
+        u32x4(&nxt)[MI] = (s & 1) ? av0 : av1;
+        if (s + 1 < 4) read_a(s + 1, nxt);
+#pragma unroll
+        for (int j = 0; j < NJW; ++j) {
+          const u32x4 b = codes_to_bf16(bq[j][s]);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            if (i < ML) acc[i][j] = mfma32(cur[i], b, acc[i][j]);
+        }
       }
     }
-  }
+  };
+  // exactly one instance runs on every path: each takes part in every barrier
+  // (live_mi = 0 -- no row of this wave in the tile -- runs the 1-block one)
+  if (live_mi >= MI)
+    main_loop(std::integral_constant<int, MI>{});
+  else if (live_mi == 3)
+    main_loop(std::integral_constant<int, 3>{});
+  else if (live_mi == 2)
+    main_loop(std::integral_constant<int, 2>{});
+  else
+    main_loop(std::integral_constant<int, 1>{});
 
   // epilogue; accumulator element e of lane l is row 8(e/4) + 4(l/32) + e%4, column l%32.
   // Results go through LDS (the stage ring is free once every wave is past
@@ -441,9 +469,9 @@ void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& 
   a.z0 = w.z_down;
   a.y = reinterpret_cast<uint16_t*>(ws + p.y);
   a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
-  if (c.d_model % 256 == 0) {
-    prefill_gemm_kernel<false, 4, kPrefillDownStages, kPrefillDownBlocks, kPrefillDownWaves, kPrefillDownWaves>
-        <<<dim3(c.d_model / 256, p.max_tiles), 64 * kPrefillDownWaves, 0, s>>>(a);
+  if (c.d_model % (64 * MOE_PF_DN_NJ) == 0) {
+    prefill_gemm_kernel<false, MOE_PF_DN_NJ, kPrefillDownStages, kPrefillDownBlocks, MOE_PF_DN_WN, kPrefillDownWaves>
+        <<<dim3(c.d_model / (64 * MOE_PF_DN_NJ), p.max_tiles), 64 * kPrefillDownWaves, 0, s>>>(a);
   } else {
     prefill_gemm_kernel<false, 2, 2, 2, 2, 4><<<dim3(c.d_model / 128, p.max_tiles), 256, 0, s>>>(a);
   }
