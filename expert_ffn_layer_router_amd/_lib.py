@@ -70,6 +70,7 @@ def load():
         "moe_create": (c_int, [ctypes.POINTER(MoeConfig), ctypes.POINTER(vp)]),
         "moe_destroy": (None, [vp]),
         "moe_workspace_size": (c_int, [vp, i32, ctypes.POINTER(sz)]),
+        "moe_control_bytes": (c_int, [vp, ctypes.POINTER(sz)]),
         "moe_forward": (c_int, [vp, i32, vp, vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp, sz, vp]),
         "moe_routing_view": (c_int, [vp, vp, i32, ctypes.POINTER(MoeRouting)]),
         "moe_graph_capture": (c_int, [vp, i32, vp, vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp, sz, vp]),

@@ -120,7 +120,8 @@ void make_plan(const moe_config& c, int T, Plan* p) {
     return at;
   };
   const size_t R = (size_t)p->R;
-  // control words: [0] router ticket, [1 + i] combine ticket of output column slice i
+  // control words, laid out the same for every T: [0] router ticket,
+  // [1 + i] combine ticket of output column slice i
   p->ctrl = take(4 * (1 + (size_t)c.d_model / kStreamCols));
   p->ctrl_bytes = off;  // aligned end of the control words (they start at offset 0)
   p->flags = take(4);
@@ -259,6 +260,16 @@ MOE_EXPORT void moe_destroy(moe_handle h) {
   drop_events(h);
   h->magic = 0;
   delete h;
+}
+
+MOE_EXPORT moe_status moe_control_bytes(moe_handle h, size_t* bytes) {
+  moe_status st = check_handle(h);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  moe::Plan p;
+  moe::make_plan(h->cfg, 0, &p);
+  *bytes = p.ctrl_bytes;
+  return MOE_OK;
 }
 
 MOE_EXPORT moe_status moe_workspace_size(moe_handle h, int32_t T, size_t* bytes) {

@@ -75,6 +75,12 @@ class MoeLayer:
         _lib.check(self.lib.moe_workspace_size(self.handle, int(T), ctypes.byref(n)))
         return n.value
 
+    def control_bytes(self) -> int:
+        """Bytes at the start of a workspace holding control words (kept zero)."""
+        n = ctypes.c_size_t()
+        _lib.check(self.lib.moe_control_bytes(self.handle, ctypes.byref(n)))
+        return n.value
+
     def new_workspace(self, T: int, device="cuda"):
         """A zero-filled workspace (the library's control words must start at zero)."""
         torch = _torch()

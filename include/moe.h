@@ -109,6 +109,11 @@ void moe_destroy(moe_handle h);
 /* Bytes of workspace a forward with T tokens needs (0 <= T <= max_tokens). */
 moe_status moe_workspace_size(moe_handle h, int32_t T, size_t *bytes);
 
+/* Bytes at the start of every workspace of this handle that hold control
+ * words (completion tickets): the same for every T, zero before first use and
+ * left zero by every call. */
+moe_status moe_control_bytes(moe_handle h, size_t *bytes);
+
 /* Enqueues the layer forward for T tokens (0 <= T <= max_tokens; T = 0 is a
  * no-op returning MOE_OK).
  *   hidden       bf16 [T][d_model]

@@ -76,6 +76,21 @@ def test_workspace_size(lib):
     lib.moe_destroy(h)
 
 
+def test_control_bytes(lib):
+    st, h = _create(lib, max_tokens=4096)
+    assert st == 0
+    n = ctypes.c_size_t()
+    assert lib.moe_control_bytes(h, ctypes.byref(n)) == 0
+    assert n.value > 0 and n.value % 256 == 0
+    for T in (1, 64, 4096):  # the control words lead every workspace
+        w = ctypes.c_size_t()
+        assert lib.moe_workspace_size(h, T, ctypes.byref(w)) == 0
+        assert n.value < w.value
+    assert lib.moe_control_bytes(None, ctypes.byref(n)) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_control_bytes(h, None) == _lib.MOE_ERR_INVALID_ARG
+    lib.moe_destroy(h)
+
+
 FAKE = 0x10000  # an aligned address that validation never dereferences
 
 

@@ -104,12 +104,13 @@ def test_small_special_shapes(E, k):
         assert np.all(np.sort(res["topk_idx"], axis=1) == np.arange(E))
 
 
-def test_out_of_range_slot_sets_flag_and_contributes_zero():
+@pytest.mark.parametrize("T", [16, 300])
+def test_out_of_range_slot_sets_flag_and_contributes_zero(T):
     require_gpu()
-    case = synth.make_case("tiny")
+    case = synth.make_case("tiny", T=T)
     table = case.weights.slot_table.copy()
     table[2] = 1000
-    say("tiny: bad slot")
+    say(f"tiny: bad slot, T={T}")
     res = gpu_layer(case).run(case.hidden, slot_table=table)
     assert res["flags"] & 1
     ref = _oracle(case, slot_table=table)
@@ -199,8 +200,9 @@ def test_zero_tokens_is_a_noop():
 
 
 def test_one_workspace_across_token_counts_keeps_control_words_zero():
-    """The fused kernels' completion tickets live at the start of the workspace;
-    every call must leave them zero, whatever T the previous call had."""
+    """The fused kernels' completion tickets live at the start of the workspace
+    (moe_control_bytes of them); every call must leave them zero, whatever T
+    the previous call had."""
     torch = require_gpu()
     case0 = synth.make_case("fine_tiny")
     g = gpu_layer(case0)
@@ -211,7 +213,7 @@ def test_one_workspace_across_token_counts_keeps_control_words_zero():
         x = g.hidden(case.hidden)
         out = g.layer.forward(x, g.router_w, g.router_b, g.slot_table, g.dw, workspace=ws)
         torch.cuda.synchronize()
-        assert int(ws[:256].abs().sum().item()) == 0, f"control words not cleared after T={T}"
+        assert int(ws[:g.layer.control_bytes()].abs().sum().item()) == 0, f"control words not cleared after T={T}"
         ref = _oracle(case)
         from gpu_util import bf16_bits_to_f64
         assert_out_close(bf16_bits_to_f64(out), ref["out"])
