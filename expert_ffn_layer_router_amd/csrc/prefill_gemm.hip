@@ -59,6 +59,9 @@ constexpr int kPrefillDownStages = MOE_PF_DN_STAGES, kPrefillDownBlocks = MOE_PF
 #ifndef MOE_PF_GU_NW
 #define MOE_PF_GU_NW 8
 #endif
+#ifndef MOE_PF_GU_WN
+#define MOE_PF_GU_WN MOE_PF_GU_NW
+#endif
 #ifndef MOE_PF_DN_NW
 #define MOE_PF_DN_NW 4
 #endif
@@ -447,7 +450,7 @@ void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* h
   a.hparts = gateup_blocks(c);
   dim3 grid(a.hparts, p.max_tiles);
   if (gateup_wide(c))
-    prefill_gemm_kernel<true, kPrefillGateUpNJ, kPrefillGateUpStages, kPrefillGateUpBlocks, kPrefillGateUpWaves,
+    prefill_gemm_kernel<true, kPrefillGateUpNJ, kPrefillGateUpStages, kPrefillGateUpBlocks, MOE_PF_GU_WN,
                         kPrefillGateUpWaves><<<grid, 64 * kPrefillGateUpWaves, 0, s>>>(a);
   else
     prefill_gemm_kernel<true, 4, 2, 2, 4, 4><<<grid, 256, 0, s>>>(a);
