@@ -83,9 +83,10 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   const int E = c.num_experts;
   if (T <= kStreamMaxTokens) {
     p->family = GemmFamily::kStream;
-    // 16-row tiles: skewed groups get more tiles (their weights then come
-    // mostly from L2 / MALL) instead of staging mostly empty activation rows
-    p->tile_rows = kStreamTileRows;
+    // tiles of 16 rows; of 32 once an expert can have more than 16 rows (each
+    // token picks an expert at most once), so that its weights are streamed
+    // once for up to 32 of them
+    p->tile_rows = T > kStreamTileRows * MOE_STREAM_RG2_MIN_T_FACTOR ? 2 * kStreamTileRows : kStreamTileRows;
   } else {
     p->family = GemmFamily::kPrefill;
     p->tile_rows = kPrefillTileRows;

@@ -31,6 +31,9 @@ constexpr int kStreamMaxTokens = 64;   // up to this T the decode (weight-stream
 constexpr int kStreamCols = 64;                     // decode family: narrowest block (64 output columns)
 constexpr int kStreamMaxNCW = MOE_STREAM_NCW;       // decode family: widest block, 64 x this many columns
 constexpr int kStreamTileRows = 16;                 // decode family: rows of an expert group per tile
+#ifndef MOE_STREAM_RG2_MIN_T_FACTOR
+#define MOE_STREAM_RG2_MIN_T_FACTOR 1                   // 32-row decode tiles once T exceeds 16 x this
+#endif
 constexpr int kDownStreamBlocks = MOE_DOWN_BLOCKS;  // k-split the decode down GEMM up to about this many blocks
 #ifndef MOE_STREAM_NCW_DOWN
 #define MOE_STREAM_NCW_DOWN MOE_STREAM_NCW

@@ -161,11 +161,15 @@ __device__ void fused_combine_tail(const StreamArgs& a, int bx, int ntiles) {
 #ifndef MOE_STREAM_WPE
 #define MOE_STREAM_WPE 4
 #endif
-template <bool GATEUP, int NCW, int NBUF, int KW, bool NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_STREAM_WPE)))
+// RG row groups of 16 per tile (tiles of up to 16 RG rows of one expert): a
+// widened weight fragment then feeds RG matrix-core products, so an expert's
+// weights are streamed once for up to 16 RG of its rows.
+template <bool GATEUP, int NCW, int NBUF, int KW, bool NT, int RG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RG == 1 ? MOE_STREAM_WPE : 3)))
 void stream_gemm_kernel(StreamArgs a) {
   static_assert(NBUF == 2 || NBUF == 3, "stage ring of 2 or 3 buffers");
   static_assert(KW == 2 || KW == 4, "k split over 2 or 4 waves");
+  static_assert(RG == 1 || RG == 2, "tiles of 16 or 32 rows");
   constexpr int COLS = 64 * NCW;                        // output columns per block
   constexpr int NWR = (GATEUP ? 2 : 1) * COLS;          // weight rows per stage
   constexpr int WBYTES = NWR * kWRowBytes;              // one stage buffer
@@ -186,7 +190,7 @@ void stream_gemm_kernel(StreamArgs a) {
   const int lr = lane & 15, grp = lane >> 4;
   const int kp = wave % KW, cp = wave / KW;
   const int n0 = bx * COLS;
-  const int4 td = a.tiles[tile];  // (expert, slot, first grouped row, rows <= 16)
+  const int4 td = a.tiles[tile];  // (expert, slot, first grouped row, rows <= 16 RG)
   const int slot = td.y, pbase = td.z, rows = td.w;
   const int ncols_total = GATEUP ? a.dff : a.d;
   const int K = GATEUP ? a.d : a.kchunk;
@@ -200,12 +204,16 @@ void stream_gemm_kernel(StreamArgs a) {
     if (GATEUP) return;
     for (int i = threadIdx.x; i < rows * COLS; i += 256) store_coherent(&yrow[(size_t)(i / COLS) * a.d + n0 + i % COLS], 0.0f);
   } else {
-    // this lane's activation row (row lr of the tile) and k offset in every
-    // stage: KR kp + (KR / 4) grp, KS x 8 values
-    const int mm = lr < rows ? lr : 0;
+    // this lane's activation rows (row lr + 16 g of the tile) and k offset in
+    // every stage: KR kp + (KR / 4) grp, KS x 8 values
     const int ka = KR * kp + (KR / 4) * grp;
-    const uint16_t* asrc = GATEUP ? a.act + (size_t)(a.perm[pbase + mm] / a.topk) * a.d + ka
-                                  : a.act + (size_t)(pbase + mm) * a.dff + kbeg + ka;
+    const uint16_t* asrc[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      const int mm = lr + 16 * g < rows ? lr + 16 * g : 0;
+      asrc[g] = GATEUP ? a.act + (size_t)(a.perm[pbase + mm] / a.topk) * a.d + ka
+                       : a.act + (size_t)(pbase + mm) * a.dff + kbeg + ka;
+    }
     const uint8_t* wsrc[WI];
 #pragma unroll
     for (int j = 0; j < WI; ++j) {
@@ -232,20 +240,27 @@ void stream_gemm_kernel(StreamArgs a) {
         load_lds16<NT>(wsrc[j] + (size_t)st * kWRowBytes - back, buf + (wave * WI + j) * 1024);
       }
     };
-    auto load_a = [&](int st, u32x4* av) {
+    auto load_a = [&](int st, u32x4 (&av)[RG][KS]) {
       const int sa = (half_last && st == nst - 1 && idle_half) ? 0 : st;
-      const u32x4* src = reinterpret_cast<const u32x4*>(asrc + (size_t)sa * kStageK);
 #pragma unroll
-      for (int j = 0; j < KS; ++j) av[j] = src[j];
+      for (int g = 0; g < RG; ++g) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(asrc[g] + (size_t)sa * kStageK);
+#pragma unroll
+        for (int j = 0; j < KS; ++j) av[g][j] = src[j];
+      }
     };
 
-    f32x4 acc[NB], accs = {0, 0, 0, 0};
+    f32x4 acc[RG][NB], accs[RG];
 #pragma unroll
-    for (int t = 0; t < NB; ++t) acc[t] = f32x4{0, 0, 0, 0};
+    for (int g = 0; g < RG; ++g) {
+      accs[g] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < NB; ++t) acc[g][t] = f32x4{0, 0, 0, 0};
+    }
     const u32x4 ones = ones_bf16();
     // this lane's bytes of every weight row: (KR / 8) bytes at KR / 2 kp + (KR / 8) grp
     const int boff = (KR / 2) * kp + (KR / 8) * grp;
-    auto compute = [&](int st, const u32x4* acur) {
+    auto compute = [&](int st, const u32x4 (&acur)[RG][KS]) {
       if (half_last && st == nst - 1 && idle_half) return;
       const char* buf = smem + (st % NBUF) * WBYTES;
       uint32_t bw[NB][KS];
@@ -266,16 +281,22 @@ void stream_gemm_kernel(StreamArgs a) {
       for (int t = 0; t < NB; ++t)
 #pragma unroll
         for (int j = 0; j < KS; ++j) lds_ready(bw[t][j]);
-      u32x4 x[KS];
+      u32x4 x[RG][KS];
 #pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        x[j] = GATEUP ? permute_a(acur[j]) : acur[j];  // h is stored in fragment order already
-        accs = mfma16(x[j], ones, accs);
-      }
+      for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+          x[g][j] = GATEUP ? permute_a(acur[g][j]) : acur[g][j];  // h is stored in fragment order already
+          accs[g] = mfma16(x[g][j], ones, accs[g]);
+        }
 #pragma unroll
       for (int t = 0; t < NB; ++t)
 #pragma unroll
-        for (int j = 0; j < KS; ++j) acc[t] = mfma16(x[j], codes_to_bf16(bw[t][j]), acc[t]);
+        for (int j = 0; j < KS; ++j) {
+          const u32x4 b = codes_to_bf16(bw[t][j]);
+#pragma unroll
+          for (int g = 0; g < RG; ++g) acc[g][t] = mfma16(x[g][j], b, acc[g][t]);
+        }
     };
 
     // Issue order: A(0), W(0) .. W(NBUF - 2); then at stage s, A(s + 1) and
@@ -283,15 +304,17 @@ void stream_gemm_kernel(StreamArgs a) {
     // A(s + 1) and W(s + 1) (NBUF = 2), or W(s + 1), A(s + 1) and W(s + 2)
     // (NBUF = 3), so waiting until that many are pending completes W(s).
     // The last NBUF - 1 stages issue no weight copies and wait for all.
-    constexpr int kPending = (NBUF - 1) * WI + KS;
-    u32x4 anx[KS], acur[KS];
+    constexpr int kPending = (NBUF - 1) * WI + RG * KS;
+    u32x4 anx[RG][KS], acur[RG][KS];
     load_a(0, anx);
     issue_w(0);
     if (NBUF == 3 && nst > 1) issue_w(1);
     const int nmain = max(0, nst - (NBUF - 1));
     for (int st = 0; st < nmain; ++st) {
 #pragma unroll
-      for (int j = 0; j < KS; ++j) acur[j] = anx[j];
+      for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int j = 0; j < KS; ++j) acur[g][j] = anx[g][j];
       load_a(st + 1, anx);
       issue_w(st + NBUF - 1);
       wait_vmem<kPending>();
@@ -311,7 +334,9 @@ void stream_gemm_kernel(StreamArgs a) {
     }
     for (int st = nmain; st < nst; ++st) {
 #pragma unroll
-      for (int j = 0; j < KS; ++j) acur[j] = anx[j];
+      for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int j = 0; j < KS; ++j) acur[g][j] = anx[g][j];
       if (st + 1 < nst) load_a(st + 1, anx);
       wait_vmem<0>();
       lds_barrier();
@@ -320,37 +345,44 @@ void stream_gemm_kernel(StreamArgs a) {
     }
 
     // Every wave turns its k part into s (acc - (128 + z) sum_k a) -- linear
-    // in the k parts -- and hands it over through LDS (the ring is free);
-    // the KW waves of a column part then add the k parts in fixed order, each
-    // for the column tiles it owns (local tile tl with tl % KW == kp).
+    // in the k parts -- and hands it over through LDS (the ring is free, one
+    // row group at a time); the KW waves of a column part then add the k
+    // parts in fixed order, each for the column tiles it owns (local tile tl
+    // with tl % KW == kp).
     float* part = reinterpret_cast<float*>(smem);  // [wave][tile][4][64]
     static_assert(4 * NB * 4 * 64 * 4 <= NBUF * WBYTES, "the k-part hand-over fits the stage ring");
-#pragma unroll
-    for (int t = 0; t < NB; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[((wave * NB + t) * 4 + i) * 64 + lane] = sc[t] * (acc[t][i] - cc[t] * accs[i]);
-    __syncthreads();
     uint16_t* hrow = GATEUP ? a.h + (size_t)pbase * a.dff + n0 : nullptr;
     float* ybase = GATEUP ? nullptr : yrow + n0;
-    for (int tl = kp; tl < CT; tl += KW) {
-      const int nl = 16 * (CT * cp + tl) + lr;
-      float v0[4] = {0, 0, 0, 0}, v1[4] = {0, 0, 0, 0};
-      for (int q = 0; q < KW; ++q) {
-        const int wq = cp * KW + q;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      if (16 * g >= rows) break;  // block-uniform
+      if (g > 0) __syncthreads();  // the previous group's hand-over is read
+#pragma unroll
+      for (int t = 0; t < NB; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          part[((wave * NB + t) * 4 + i) * 64 + lane] = sc[t] * (acc[g][t][i] - cc[t] * accs[g][i]);
+      __syncthreads();
+      for (int tl = kp; tl < CT; tl += KW) {
+        const int nl = 16 * (CT * cp + tl) + lr;
+        float v0[4] = {0, 0, 0, 0}, v1[4] = {0, 0, 0, 0};
+        for (int q = 0; q < KW; ++q) {
+          const int wq = cp * KW + q;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v0[i] += part[((wq * NB + tl) * 4 + i) * 64 + lane];
+            if (GATEUP) v1[i] += part[((wq * NB + CT + tl) * 4 + i) * 64 + lane];
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v0[i] += part[((wq * NB + tl) * 4 + i) * 64 + lane];
-          if (GATEUP) v1[i] += part[((wq * NB + CT + tl) * 4 + i) * 64 + lane];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = grp * 4 + i;
-        if (row < rows) {
-          if (GATEUP)
-            hrow[(uint32_t)(row * a.dff + h_phys_col(nl))] = f32_to_bf16(silu(v0[i]) * v1[i]);
-          else
-            store_coherent(&ybase[(uint32_t)(row * a.d + nl)], v0[i]);
+          const int row = 16 * g + grp * 4 + i;
+          if (row < rows) {
+            if (GATEUP)
+              hrow[(uint32_t)(row * a.dff + h_phys_col(nl))] = f32_to_bf16(silu(v0[i]) * v1[i]);
+            else
+              store_coherent(&ybase[(uint32_t)(row * a.d + nl)], v0[i]);
+          }
         }
       }
     }
@@ -379,7 +411,10 @@ void launch_stream(const moe_config& c, const Plan& p, const StreamArgs& args, h
   const int ncols = GATEUP ? c.d_ff : c.d_model;
   dim3 grid(ncols / (64 * NCW), p.max_tiles, GATEUP ? 1 : p.down_split);
   constexpr int KW = GATEUP ? MOE_STREAM_KW_GU : MOE_STREAM_KW_DN;
-  stream_gemm_kernel<GATEUP, NCW, MOE_STREAM_NBUF, KW, true><<<grid, 256, 0, s>>>(args);
+  if (p.tile_rows == 2 * kStreamTileRows)
+    stream_gemm_kernel<GATEUP, NCW, MOE_STREAM_NBUF, KW, true, 2><<<grid, 256, 0, s>>>(args);
+  else
+    stream_gemm_kernel<GATEUP, NCW, MOE_STREAM_NBUF, KW, true, 1><<<grid, 256, 0, s>>>(args);
 }
 }  // namespace
 
