@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_hip.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["router.hip", "permute.hip", "stream_gemm.hip", "prefill_gemm.hip", "combine.hip", "moe_api.hip"]
+SOURCES = ["router.hip", "permute.hip", "stream_gemm.hip", "prefill_gemm.hip", "combine.hip", "moe_api.hip",
+           "expert_cache.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

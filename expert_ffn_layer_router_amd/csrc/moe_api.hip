@@ -40,13 +40,18 @@ constexpr uint32_t kMagic = 0x4d6f4531u;  // "MoE1"
 
 thread_local std::string g_last_error;
 
-moe_status fail(moe_status st, const char* fmt, ...) {
+moe_status vfail(moe_status st, const char* fmt, va_list ap) {
   char buf[512];
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status fail(moe_status st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vfail(st, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return st;
 }
 
@@ -73,6 +78,22 @@ struct moe_layer {
   int timing_capacity = 0;
   int timing_recorded = 0;
 };
+
+namespace moe {
+// Error reporting and handle checks shared with the library's other host sources.
+moe_status api_fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(st, fmt, ap);
+  va_end(ap);
+  return st;
+}
+bool api_check_handle(moe_handle h, const moe_config** cfg) {
+  if (!h || h->magic != kMagic) return false;
+  *cfg = &h->cfg;
+  return true;
+}
+}  // namespace moe
 
 namespace moe {
 

@@ -150,8 +150,79 @@ class MoeLayer:
         _lib.check(self.lib.moe_stage_times(self.handle, ms, _lib.MOE_NUM_STAGES, ctypes.byref(n)))
         return dict(zip(_lib.STAGE_NAMES, [float(v) for v in ms])), int(n.value)
 
+    def upload_expert(self, pool: DeviceWeights, slot: int, src: "HostExpert", stream=None) -> None:
+        """Enqueues the copies of one expert (host buffers) into pool slot `slot`."""
+        _lib.check(self.lib.moe_expert_upload(self.handle, ctypes.byref(pool.struct()), int(slot),
+                                              ctypes.byref(src.struct()), self._stream(stream)))
+
     def device_flags(self, workspace, T: int, stream=None) -> int:
         f = ctypes.c_uint32()
         _lib.check(self.lib.moe_device_flags(self.handle, _ptr(workspace), int(T), self._stream(stream),
                                              ctypes.byref(f)))
         return int(f.value)
+
+
+@dataclasses.dataclass
+class HostExpert:
+    """One expert's weights in page-locked host memory (the pool layout with a
+    single slot), the source of moe_expert_upload."""
+    tensors: dict
+
+    @classmethod
+    def from_pool(cls, weights, expert_slot: int) -> "HostExpert":
+        torch = _torch()
+        src = weights if isinstance(weights, dict) else {f: getattr(weights, f) for f in WEIGHT_FIELDS}
+        out = {}
+        for f in WEIGHT_FIELDS:
+            a = np.ascontiguousarray(src[f][expert_slot])
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            t = torch.empty(a.shape, dtype=torch.from_numpy(a[:0]).dtype, pin_memory=True)
+            t.copy_(torch.from_numpy(a))
+            out[f] = t
+        return cls(out)
+
+    def struct(self) -> _lib.MoeWeights:
+        return _lib.MoeWeights(**{f: _ptr(self.tensors[f]) for f in WEIGHT_FIELDS})
+
+
+class ExpertCache:
+    """The library's set-associative LRU cache of (layer, expert) over pool slots."""
+
+    def __init__(self, num_sets: int, ways: int, num_experts: int):
+        self.lib = _lib.load()
+        self.num_experts = num_experts
+        h = ctypes.c_void_p()
+        _lib.check(self.lib.moe_cache_create(int(num_sets), int(ways), int(num_experts), ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.moe_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def request(self, layer: int, experts):
+        """(slots of `experts`, [(expert, slot) to load], slot table of the layer)."""
+        ex = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+        n = int(ex.size)
+        slots = np.zeros(max(n, 1), np.int32)
+        le = np.zeros(max(n, 1), np.int32)
+        ls = np.zeros(max(n, 1), np.int32)
+        table = np.zeros(self.num_experts, np.int32)
+        nl = ctypes.c_int32()
+        p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+        _lib.check(self.lib.moe_cache_request(self.handle, int(layer), p(ex), n, p(slots), p(le), p(ls),
+                                              ctypes.byref(nl), p(table)))
+        return ([int(v) for v in slots[:n]], [(int(le[i]), int(ls[i])) for i in range(nl.value)],
+                [int(v) for v in table])
+
+    def stats(self):
+        h, m = ctypes.c_int64(), ctypes.c_int64()
+        _lib.check(self.lib.moe_cache_stats(self.handle, ctypes.byref(h), ctypes.byref(m)))
+        return int(h.value), int(m.value)

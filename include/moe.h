@@ -171,6 +171,58 @@ const char *moe_status_string(moe_status s);
 /* Detail of the calling thread's last failing call ("" if none). */
 const char *moe_last_error(void);
 
+/* ---- Expert slot cache and slot refill ------------------------------------
+ * Co-inference page, section 2.2: the weight pool's slots form an N-way
+ * set-associative cache of (layer, expert) weights -- M ways per set,
+ * N = S / M sets -- with LRU replacement.  Section 3.1 and the Strata page,
+ * section 2.2: the experts a layer will need are copied host -> device on a
+ * second stream while the GPU computes.  The cache only decides which slot
+ * holds which expert (host bookkeeping, no device call); the caller enqueues
+ * the copies it asks for with moe_expert_upload, orders them before the
+ * forward that uses them (an event between the streams), and writes the slot
+ * table the request returns to the device. */
+typedef struct moe_cache *moe_cache_handle;
+
+/* A cache of num_sets x ways slots (slot = set * ways + way) over experts
+ * 0 .. num_experts - 1 of any number of layers.  MOE_ERR_INVALID_ARG unless
+ * all three are positive and there are at most 2^24 slots. */
+moe_status moe_cache_create(int32_t num_sets, int32_t ways, int32_t num_experts, moe_cache_handle *out);
+
+/* Frees the cache.  NULL is ignored. */
+void moe_cache_destroy(moe_cache_handle c);
+
+/* Makes the n experts in `experts` (duplicates allowed) of layer `layer`
+ * (>= 0) resident in the layer's set, layer mod num_sets.  Resident ones are
+ * hits.  Each missing one takes an empty way of the set (lowest first), else
+ * the least recently used way that holds no expert of this request (lowest
+ * way among equals), evicting its expert; then every expert of the request
+ * counts as used now.
+ *   slots         [n] receives the slot of experts[i]
+ *   load_experts,
+ *   load_slots    [n] receive the experts that were not resident and their
+ *                 new slots (*n_loads of them): copy those before use
+ *   slot_table    [num_experts] or NULL: receives the layer's slot table, the
+ *                 slot of every resident expert and -1 elsewhere (a forward
+ *                 treats -1 as missing: the expert contributes zero and
+ *                 MOE_FLAG_BAD_SLOT is raised)
+ * MOE_ERR_INVALID_ARG for an expert out of range or more distinct experts
+ * than ways; the cache is then unchanged. */
+moe_status moe_cache_request(moe_cache_handle c, int32_t layer, const int32_t *experts, int32_t n, int32_t *slots,
+                             int32_t *load_experts, int32_t *load_slots, int32_t *n_loads, int32_t *slot_table);
+
+/* Hits and misses over all requests so far. */
+moe_status moe_cache_stats(moe_cache_handle c, int64_t *hits, int64_t *misses);
+
+/* Enqueues on `stream` the copies of one expert's weights into pool slot
+ * `slot` (0 <= slot < num_slots): `src` holds that expert alone, in the
+ * moe_weights layout with a single slot, in host memory (page-locked, for the
+ * copies to run asynchronously) or device memory.  Nothing is allocated; the
+ * source must stay valid until the copies complete.  The caller orders the
+ * copies before any forward that reads the slot (and after any still
+ * reading the expert it replaces). */
+moe_status moe_expert_upload(moe_handle h, const moe_weights *pool, int32_t slot, const moe_weights *src,
+                             moe_stream stream);
+
 #ifdef __cplusplus
 }
 #endif
