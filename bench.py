@@ -14,6 +14,7 @@ model's successive layers have different weights).
 
 Extra modes for counter runs:
     --copy-calibration   time a plain 1 GiB device copy (scale for FETCH/WRITE_SIZE)
+    --refill             time expert uploads into pool slots, alone and beside the steps
     --summarize-pmc DIR  fold a rocprofv3 --pmc output directory into a JSON summary
 """
 
@@ -186,6 +187,66 @@ def copy_calibration(gib=1.0, reps=5):
 
 
 # --------------------------------------------------------------------------- main bench
+def run_refill(args, shape, w, pools, layer, step, stream, torch):
+    """Slot-pool refill: one expert's weights copied from page-locked host
+    memory into a pool slot on a copy stream (moe_expert_upload), timed alone,
+    and beside the layer steps on the compute stream.  The copies rewrite
+    slots 0 and 1 with the experts they already hold, so the steps compute
+    the same layer.  Prints one JSON line."""
+    from expert_ffn_layer_router_amd import HostExpert
+    d, f = shape.d_model, shape.d_ff
+    expert_bytes = 3 * d * f // 2 + 2 * (4 * f + 2 * d)
+    host = [HostExpert.from_pool(w, e) for e in (0, 1)]
+    copy = torch.cuda.Stream()
+    n_up = 8
+
+    def uploads(n):
+        for i in range(n):
+            layer.upload_expert(pools[0], i % 2, host[i % 2], stream=copy)
+
+    uploads(2)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(copy)
+    uploads(n_up)
+    c1.record(copy)
+    torch.cuda.synchronize()
+    up_alone = c0.elapsed_time(c1) / n_up
+    log(f"refill: one expert ({expert_bytes / 1e6:.1f} MB) uploads in {up_alone * 1e3:.0f} us alone")
+
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        s0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        s1.record(stream)
+    torch.cuda.synchronize()
+    step_alone = s0.elapsed_time(s1) / args.steps
+    # beside the steps: enough uploads to cover the steps
+    n_bg = max(2, int(step_alone * args.steps / max(up_alone, 1e-3)) + 1)
+    c0.record(copy)
+    uploads(n_bg)
+    c1.record(copy)
+    with torch.cuda.stream(stream):
+        s0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        s1.record(stream)
+    torch.cuda.synchronize()
+    step_beside = s0.elapsed_time(s1) / args.steps
+    up_beside = c0.elapsed_time(c1) / n_bg
+    log(f"refill: step {step_alone * 1e3:.1f} us alone, {step_beside * 1e3:.1f} us beside uploads; "
+        f"upload {up_beside * 1e3:.0f} us beside steps")
+    print(json.dumps({
+        "metric": "expert refill (host -> pool slot) beside layer steps", "config": {"workload": args.config},
+        "expert_bytes": expert_bytes, "upload_us_alone": up_alone * 1e3,
+        "upload_gbs_alone": expert_bytes / (up_alone * 1e-3) / 1e9,
+        "upload_us_beside_steps": up_beside * 1e3, "upload_gbs_beside_steps": expert_bytes / (up_beside * 1e-3) / 1e9,
+        "step_us_alone": step_alone * 1e3, "step_us_beside_uploads": step_beside * 1e3,
+        "steps": args.steps, "uploads_beside": n_bg}))
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +260,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--refill", action="store_true",
+                    help="time expert uploads (host -> slot) alone and beside the layer steps")
     ap.add_argument("--summarize-pmc", metavar="DIR", nargs="+", help="rocprofv3 --pmc output directories")
     ap.add_argument("--copy-pmc", metavar="DIR", nargs="*", default=[], help="--pmc runs of --copy-calibration")
     ap.add_argument("--pmc-out", metavar="JSON")
@@ -294,6 +357,9 @@ def main(argv=None):
             step(i)
     stream.synchronize()
     torch.cuda.synchronize()
+
+    if args.refill:
+        return run_refill(args, shape, w, pools, layers[0], step, stream, torch)
 
     # timed region: K whole-layer steps
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
