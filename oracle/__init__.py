@@ -12,12 +12,16 @@ route evaluates faster):
     FFN_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x)),   silu(z) = z / (1 + exp(-z))
     W_hat    = (q - z) * s       per output row, codes q in [0, 15]
 
-with the weights of expert e read from pool slot slot_table[e].
+with the weights of expert e read from pool slot slot_table[e].  Shared
+experts E .. E + S - 1 (if any) are added for every token with weight 1:
+
+    out[t] += sum over s < S of FFN_{E+s}(x[t])
 
 Sources (page titles abbreviated; the pages are the three web pages on
 expert offloading for MoE inference):
   * Strata page ("125B MoE at 100+ tok/s on an RTX 3090"):
       section 1.1 -- the router picks the top-2 (or top-1) experts per token;
+      section 2.1 -- the shared expert stays resident next to the routed ones;
       section 3.1 -- per-expert int4 with its own scale and zero-point,
                      dequantised to 16-bit before the matrix cores;
       section 3.2 -- the expert FFN is a two-layer MLP, evaluated as a group
@@ -29,7 +33,9 @@ expert offloading for MoE inference):
 Readings where the pages are silent (each is listed in the design notes):
 selection on fp64 logits with ties to the lower expert id; weights are the
 softmax over the k selected logits (equal to softmax-then-renormalise);
-SwiGLU experts without biases; stable regroup in expert-id order.
+SwiGLU experts without biases; stable regroup in expert-id order; a shared
+expert is one more expert every token takes with weight exactly 1, after its
+routed ones.
 
 Parity pins (tests marked "not gpu"): hand-worked closed forms, W_r = 0 and
 k = E special cases, brute-force routing and regrouping by pure-Python loops,

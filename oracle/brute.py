@@ -4,7 +4,8 @@ This takes no regrouping at all: it computes FFN_e(x) for all tokens and all
 experts and keeps w[t,e] only where e is among token t's k choices.  In exact
 arithmetic it equals the regrouped forward, so it pins the regroup, the
 per-expert row gathering and the weighted scatter-back independently of how
-those are done.  Only for tiny layers.
+those are done.  Shared experts (numbered E + s, slot slot_table[E + s]) are
+added for every token with weight 1.  Only for tiny layers.
 """
 
 import numpy as np
@@ -15,7 +16,7 @@ from .routing import route
 
 
 def brute_dense(hidden, router_w, router_b, slot_table, w_gate, w_up, w_down,
-                s_gate, z_gate, s_up, z_up, s_down, z_down, top_k):
+                s_gate, z_gate, s_up, z_up, s_down, z_down, top_k, num_shared=0):
     x = bf16_to_f64(hidden)
     T, d = x.shape
     E = np.asarray(router_w).shape[0]
@@ -34,4 +35,8 @@ def brute_dense(hidden, router_w, router_b, slot_table, w_gate, w_up, w_down,
             continue
         F = expert_ffn(x, slot, dtype=np.float64, **wts)
         out += mask[:, e:e + 1] * F
+    for e in range(E, E + int(num_shared)):   # shared experts: every token, weight 1
+        slot = int(slot_table[e])
+        if 0 <= slot < S:
+            out += expert_ffn(x, slot, dtype=np.float64, **wts)
     return out

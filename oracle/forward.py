@@ -17,6 +17,14 @@ activations go through fp32 BLAS; routing and the final weighting stay fp64.
 
 A slot id outside [0, num_slots) makes that expert contribute zero (the HIP
 path reports such an id through its device error flag).
+
+Shared experts (Strata page, section 2.1: the shared expert common in MoE
+models stays resident next to the routed ones).  Reading: a shared expert is
+applied to every token with weight exactly 1 and added after the routed
+experts; shared expert s is numbered E + s, its weights sit in pool slot
+slot_table[E + s], and in the routing it is one more column per token
+(topk_idx[t, k + s] = E + s, topk_w[t, k + s] = 1), so the regroup gives it a
+group of all T tokens in token order.
 """
 
 import numpy as np
@@ -48,11 +56,15 @@ def expert_ffn(X, slot, w_gate, w_up, w_down, s_gate, z_gate, s_up, z_up, s_down
 
 
 def forward(hidden, router_w, router_b, slot_table, w_gate, w_up, w_down,
-            s_gate, z_gate, s_up, z_up, s_down, z_down, top_k, precision="f64", tokens=None):
+            s_gate, z_gate, s_up, z_up, s_down, z_down, top_k, precision="f64", tokens=None,
+            num_shared=0):
     """Returns a dict with the routing, the regrouping and out (fp64).
 
     tokens: optional sorted array of token indices; out then holds only those
     rows (routing and regrouping still cover every token).
+    num_shared: shared experts after the E routed ones; slot_table then has
+    E + num_shared entries and topk_idx / topk_w have top_k + num_shared
+    columns.
     """
     dtype = {"f64": np.float64, "f32": np.float32}[precision]
     hidden = np.asarray(hidden)
@@ -61,6 +73,13 @@ def forward(hidden, router_w, router_b, slot_table, w_gate, w_up, w_down,
     E = np.asarray(router_w).shape[0]
     S = np.asarray(w_gate).shape[0]
     logits, idx, w = route(hidden, router_w, router_b, k)
+    ns = int(num_shared)
+    if ns < 0 or np.asarray(slot_table).shape[0] != E + ns:
+        raise ValueError("need num_shared >= 0 and E + num_shared slot-table entries")
+    if ns:
+        idx = np.concatenate([idx, np.broadcast_to(np.arange(E, E + ns, dtype=idx.dtype), (T, ns))], axis=1)
+        w = np.concatenate([w, np.ones((T, ns))], axis=1)
+        k, E = k + ns, E + ns
     counts, offsets, perm, inv = regroup(idx, E)
 
     tok_sel = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)

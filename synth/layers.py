@@ -18,6 +18,8 @@ in parallel):
     unsigned int4 with one fp16 scale and one integer zero-point (stored as
     fp16) per output row -- the per-expert quantisation of the Strata page,
     section 3.1;
+  * shared experts (num_shared > 0) are drawn like routed experts E, E+1, ...
+    and have no router row;
   * the pool has num_slots slots; expert e lives at slot slot_table[e];
     slots no expert uses are filled with random codes and NaN scales so that a
     wrong indirection cannot go unnoticed.
@@ -54,13 +56,14 @@ class LayerShape:
     num_experts: int
     top_k: int
     num_slots: int
-    slot_kind: str = "identity"   # identity | perm (all slots, shuffled) | sparse (E of S slots)
+    slot_kind: str = "identity"   # identity | perm (all slots, shuffled) | sparse (E + shared of S slots)
     zipf_s: float = 0.0           # 0: no router bias
+    num_shared: int = 0           # shared experts (every token, weight 1), numbered E .. E + num_shared - 1
 
     def family(self) -> tuple:
-        """Everything but T: layers that differ only in T share weights."""
+        """Everything but T and top_k: layers that differ only in those share weights."""
         return (self.d_model, self.d_ff, self.num_experts, self.num_slots,
-                self.slot_kind, float(self.zipf_s))
+                self.slot_kind, float(self.zipf_s), int(self.num_shared))
 
 
 CASES = {
@@ -76,6 +79,14 @@ CASES = {
     "fine_prefill": LayerShape(4096, 4096, 2048, 64, 6, 128, "sparse", 1.0),
     # the fine-grained routing structure at tiny width (CPU brute force)
     "fine_tiny": LayerShape(16, 128, 256, 64, 6, 128, "sparse", 1.0),
+    # top-1 routing plus one shared expert of the same shape (Mixtral-8x7B-shaped
+    # experts): a batch-16 decode step and a 2048-token prefill chunk
+    "shared_decode": LayerShape(16, 4096, 14336, 8, 1, 9, "identity", 0.0, 1),
+    "shared_prefill": LayerShape(2048, 4096, 14336, 8, 1, 9, "identity", 0.0, 1),
+    # the same structure at tiny width, and fine-grained top-6 with two shared
+    # experts (8 experts per token), both with scattered slots
+    "shared_tiny": LayerShape(16, 128, 256, 8, 1, 12, "sparse", 1.0, 1),
+    "fine_shared_tiny": LayerShape(16, 128, 256, 64, 6, 80, "sparse", 1.0, 2),
 }
 
 
@@ -88,9 +99,9 @@ def case_shape(name: str, T: Optional[int] = None) -> LayerShape:
 class Weights:
     """One layer's weights, pool-indexed by slot.  Half-precision arrays hold
     IEEE fp16 bit patterns (uint16)."""
-    router_w: np.ndarray            # fp32 [E, d]
+    router_w: np.ndarray            # fp32 [E, d] (routed experts only)
     router_b: Optional[np.ndarray]  # fp32 [E] or None
-    slot_table: np.ndarray          # int32 [E]
+    slot_table: np.ndarray          # int32 [E + num_shared]
     w_gate: np.ndarray              # uint8 [S, d_ff, d/2]
     w_up: np.ndarray                # uint8 [S, d_ff, d/2]
     w_down: np.ndarray              # uint8 [S, d, d_ff/2]
@@ -174,8 +185,9 @@ def _cache_dir() -> str:
 
 
 def _cache_key(shape: LayerShape, seed: int) -> str:
-    d, f, E, S, kind, zs = shape.family()
-    return f"v{_CACHE_VERSION}_d{d}_f{f}_E{E}_S{S}_{kind}_z{zs:g}_seed{seed}"
+    d, f, E, S, kind, zs, ns = shape.family()
+    shared = f"_sh{ns}" if ns else ""
+    return f"v{_CACHE_VERSION}_d{d}_f{f}_E{E}{shared}_S{S}_{kind}_z{zs:g}_seed{seed}"
 
 
 def _load_cached(key: str) -> Optional[Weights]:
@@ -206,13 +218,15 @@ def _store_cached(key: str, w: Weights) -> None:
 
 
 def _generate_weights(shape: LayerShape, seed: int) -> Weights:
-    d, f, E, S = shape.d_model, shape.d_ff, shape.num_experts, shape.num_slots
+    d, f, S = shape.d_model, shape.d_ff, shape.num_slots
+    Er = shape.num_experts                 # routed experts (router rows)
+    E = Er + shape.num_shared              # every expert with weights, shared ones last
     if d % 2 or f % 2:
         raise ValueError("d_model and d_ff must be even (two int4 codes per byte)")
-    router_w = _rng(seed, _ROUTER).standard_normal((E, d), dtype=np.float32) * np.float32(1 / np.sqrt(d))
+    router_w = _rng(seed, _ROUTER).standard_normal((Er, d), dtype=np.float32) * np.float32(1 / np.sqrt(d))
     router_b = None
     if shape.zipf_s:
-        router_b = (-float(shape.zipf_s) * np.log(np.arange(1, E + 1, dtype=np.float64))).astype(np.float32)
+        router_b = (-float(shape.zipf_s) * np.log(np.arange(1, Er + 1, dtype=np.float64))).astype(np.float32)
     if shape.slot_kind == "identity":
         if S < E:
             raise ValueError("identity slot table needs num_slots >= num_experts")
@@ -267,7 +281,7 @@ def _generate_weights(shape: LayerShape, seed: int) -> Weights:
 
 @lru_cache(maxsize=2)
 def _weights_memo(family: tuple, top_k: int, seed: int) -> Weights:
-    shape = LayerShape(0, family[0], family[1], family[2], top_k, family[3], family[4], family[5])
+    shape = LayerShape(0, family[0], family[1], family[2], top_k, family[3], family[4], family[5], family[6])
     big = shape.num_slots * 3 * shape.d_model * shape.d_ff // 2 > (64 << 20)
     key = _cache_key(shape, seed)
     if big:

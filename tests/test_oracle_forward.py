@@ -170,3 +170,76 @@ def test_token_subset_matches_full_forward():
     full = oracle.forward(case.hidden, top_k=6, **kw)["out"]
     sub = oracle.forward(case.hidden, top_k=6, tokens=np.array([0, 5, 15]), **kw)["out"]
     assert_out_close(sub, full[[0, 5, 15]], rel=1e-12)     # BLAS blocking depends on the row count
+
+
+# ---- shared experts (Strata page, section 2.1: a shared expert kept resident) ----
+
+def test_hand_worked_shared_expert_with_top1():
+    """One routed expert (the hand layer's expert 0, top-1, so weight 1) plus
+    the hand layer's expert 1 as a shared expert.  Token 0: FFN_0(x0) + FFN_1(x0),
+    and FFN_1(x0) = 0 (its gate rows see G = 0); token 1: FFN_0(x1) = 0 plus
+    FFN_1(x1)."""
+    hidden, w = _hand_layer()
+    Wr = np.array([[1.0, 0.0]], np.float32)
+    h0, h1 = silu(2.0), 3 * silu(-1.0)
+    g0, g1 = 2 * silu(1.0), -silu(0.5)
+    want = [[h0 + h1, 2 * h1], [-g0, 0.5 * g0 + 1.5 * g1]]
+    r = oracle.forward(hidden, Wr, None, np.array([0, 1], np.int32), top_k=1, num_shared=1, **w)
+    np.testing.assert_allclose(r["out"], want, rtol=1e-15, atol=1e-15)
+    assert r["topk_idx"].tolist() == [[0, 1], [0, 1]]
+    assert r["topk_w"].tolist() == [[1.0, 1.0], [1.0, 1.0]]
+    assert r["counts"].tolist() == [2, 2] and r["offsets"].tolist() == [0, 2, 4]
+    assert r["perm"].tolist() == [0, 2, 1, 3] and r["inv"].tolist() == [0, 2, 1, 3]
+
+
+@pytest.mark.parametrize("name", ["shared_tiny", "fine_shared_tiny"])
+def test_shared_forward_equals_dense_then_mask(name):
+    case = synth.make_case(name)
+    kw = weights_kwargs(case.weights)
+    k, ns = case.shape.top_k, case.shape.num_shared
+    res = oracle.forward(case.hidden, top_k=k, num_shared=ns, **kw)
+    dense = oracle.brute_dense(case.hidden, top_k=k, num_shared=ns, **kw)
+    assert_out_close(res["out"], dense, rel=1e-12)
+    E, T = case.shape.num_experts, case.shape.T
+    # every token holds the shared experts in its last columns, with weight 1
+    assert res["topk_idx"].shape == (T, k + ns)
+    assert np.all(res["topk_idx"][:, k:] == np.arange(E, E + ns))
+    assert np.all(res["topk_w"][:, k:] == 1.0)
+    assert np.all(res["topk_idx"][:, :k] < E)
+    # each shared group holds all T tokens in token order
+    for s in range(ns):
+        g = res["perm"][res["offsets"][E + s]:res["offsets"][E + s + 1]]
+        assert g.tolist() == [t * (k + ns) + k + s for t in range(T)]
+    assert res["counts"].sum() == T * (k + ns)
+
+
+def test_shared_expert_with_zero_weights_adds_nothing():
+    case = synth.make_case("shared_tiny")
+    kw = weights_kwargs(case.weights)
+    sl = int(kw["slot_table"][case.shape.num_experts])
+    kw = {a: (v.copy() if isinstance(v, np.ndarray) else v) for a, v in kw.items()}
+    for m in ("gate", "up", "down"):
+        z = kw["z_" + m][sl].view(np.float16).astype(np.uint8)
+        kw["w_" + m][sl] = oracle.pack_codes(np.repeat(z[:, None], 2 * kw["w_" + m].shape[-1], axis=1))
+    with_shared = oracle.forward(case.hidden, top_k=1, num_shared=1, **kw)["out"]
+    routed_only = oracle.forward(case.hidden, top_k=1, **dict(kw, slot_table=kw["slot_table"][:-1]))["out"]
+    np.testing.assert_array_equal(with_shared, routed_only)
+
+
+def test_shared_copy_of_the_only_expert_doubles_the_output():
+    """E = 1, top-1 (weight 1) and a shared expert in the same slot: exactly twice
+    the routed-only output."""
+    shape = synth.LayerShape(12, 128, 256, 1, 1, 1, "identity", 0.0)
+    w = synth.make_weights(shape, seed=3)
+    x = synth.make_hidden(12, 128, seed=3)
+    kw = weights_kwargs(w)
+    base = oracle.forward(x, top_k=1, **kw)["out"]
+    both = oracle.forward(x, top_k=1, num_shared=1, **dict(kw, slot_table=np.array([0, 0], np.int32)))["out"]
+    np.testing.assert_array_equal(both, 2 * base)
+
+
+def test_shared_count_must_match_the_slot_table():
+    case = synth.make_case("shared_tiny")
+    kw = weights_kwargs(case.weights)
+    with pytest.raises(ValueError):
+        oracle.forward(case.hidden, top_k=1, **kw)           # slot table has E + 1 entries
