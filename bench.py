@@ -37,7 +37,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
 DECODE_BOUND = {"mixtral_decode": "hbm", "phi35_skew": "hbm", "fine_decode": "hbm", "tiny": "hbm",
-                "fine_tiny": "hbm", "mixtral_prefill": "mfma", "fine_prefill": "mfma"}
+                "fine_tiny": "hbm", "mixtral_prefill": "mfma", "fine_prefill": "mfma",
+                "shared_decode": "hbm", "shared_prefill": "mfma", "shared_tiny": "hbm", "fine_shared_tiny": "hbm"}
 CSRC = os.path.join(ROOT, "expert_ffn_layer_router_amd", "csrc")
 STREAM_MAX_TOKENS = 64   # the library's decode (weight-streaming) family runs up to this T
 
@@ -66,15 +67,17 @@ def source_sha() -> str:
 # --------------------------------------------------------------------------- work accounting
 def algorithmic_work(shape, counts):
     """Bytes and FLOPs the method itself must move / compute for one forward,
-    per kernel and for the layer (active experts only; no tile padding)."""
-    d, f, T, k, E = shape.d_model, shape.d_ff, shape.T, shape.top_k, shape.num_experts
+    per kernel and for the layer (active experts only; no tile padding).
+    Shared experts count as experts with T rows each; `counts` covers them."""
+    d, f, T, ns = shape.d_model, shape.d_ff, shape.T, shape.num_shared
+    k, E = shape.top_k + ns, shape.num_experts          # rows per token; routed experts
     R = T * k
     active = int(sum(1 for c in counts if c > 0))
     gate_up_w = active * (d * f + 2 * 2 * 2 * f)       # gate+up codes (2 x d*f/2) + fp16 s,z of both
     down_w = active * (d * f // 2 + 2 * 2 * d)          # down codes + fp16 s,z
     gate_up_bytes = gate_up_w + 2 * T * d + 2 * R * f   # + x rows read, h written (bf16)
     down_bytes = down_w + 2 * R * f + 2 * R * d         # + h read, y written (bf16-equivalent)
-    layer_bytes = gate_up_w + down_w + 2 * T * d + 2 * T * d + 4 * E * d + 4 * E + 4 * E
+    layer_bytes = gate_up_w + down_w + 2 * T * d + 2 * T * d + 4 * E * d + 4 * E + 4 * (E + ns)
     return dict(active=active, R=R,
                 gate_up=dict(bytes=gate_up_bytes, flops=4 * R * d * f),
                 down=dict(bytes=down_bytes, flops=2 * R * d * f),
@@ -99,7 +102,8 @@ def cpu_baseline(case, budget_s=15.0):
     t_end = time.perf_counter() + budget_s
     while True:
         t0 = time.perf_counter()
-        oracle.forward(case.hidden, top_k=shape.top_k, precision="f32", tokens=tokens, **kw)
+        oracle.forward(case.hidden, top_k=shape.top_k, precision="f32", tokens=tokens,
+                       num_shared=shape.num_shared, **kw)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() > t_end or len(times) >= 5:
             break
@@ -295,7 +299,7 @@ def main(argv=None):
     case = synth.make_case(args.config)
     shape, w = case.shape, case.weights
     log(f"workload {args.config}: T={shape.T} d={shape.d_model} d_ff={shape.d_ff} E={shape.num_experts} "
-        f"k={shape.top_k} slots={shape.num_slots}")
+        f"k={shape.top_k} shared={shape.num_shared} slots={shape.num_slots}")
 
     # routing of this batch (for the work accounting)
     pool_bytes = w.nbytes()
@@ -304,7 +308,8 @@ def main(argv=None):
     rw = to_device(w.router_w)
     rb = None if w.router_b is None else to_device(w.router_b)
     st = to_device(w.slot_table)
-    probe = MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T)
+    probe = MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T,
+                     num_shared=shape.num_shared)
     ws = probe.new_workspace(T)
     out = torch.empty((T, shape.d_model), dtype=torch.bfloat16, device="cuda")
 
@@ -321,8 +326,8 @@ def main(argv=None):
     log(f"{work['active']} active experts, {active_bytes / 1e6:.1f} MB algorithmic per step, "
         f"{rot} weight-pool copies of {pool_bytes / 1e6:.1f} MB")
 
-    layers = [MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T)
-              for _ in range(rot)]
+    layers = [MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T,
+                       num_shared=shape.num_shared) for _ in range(rot)]
     stream = torch.cuda.Stream()
     multi = None
     if args.mode == "graph":
@@ -420,7 +425,8 @@ def main(argv=None):
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.config, "T": T, "d_model": shape.d_model, "d_ff": shape.d_ff,
-                   "num_experts": shape.num_experts, "top_k": shape.top_k, "num_slots": shape.num_slots,
+                   "num_experts": shape.num_experts, "top_k": shape.top_k, "num_shared": shape.num_shared,
+                   "num_slots": shape.num_slots,
                    "weights": "int4 codes + fp16 scale/zero-point per output row",
                    "mode": {"layers": f"HIP graph of {rot} consecutive layers (own weights each), replayed",
                             "graph": "one HIP graph per layer step", "eager": "eager launches"}[args.mode],

@@ -70,7 +70,10 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 struct moe_layer {
   uint32_t magic = kMagic;
-  moe_config cfg{};
+  moe_config cfg{};   // as created
+  // the shape every kernel after the router sees: shared experts are groups
+  // E .. E+S-1 and token columns k .. k+S-1 (num_experts = E + S, top_k = k + S)
+  moe_config ecfg{};
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   // stage timing: (MOE_NUM_STAGES + 1) events per recorded forward
@@ -101,7 +104,8 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   *p = Plan{};
   p->T = T;
   p->R = T * c.top_k;
-  const int E = c.num_experts;
+  const int E = c.num_experts;                  // groups: routed + shared experts
+  const int Er = c.num_experts - c.num_shared;  // rows of the router
   if (T <= kStreamMaxTokens) {
     p->family = GemmFamily::kStream;
     // tiles of 16 rows; of 32 once an expert can have more than 16 rows (each
@@ -120,7 +124,7 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   } else {
     // 64-token x router_tile_experts(E) tiles; split k (in multiples of 32) until about 512 blocks
     const int tiles = ((T + kRouterMfmaTokens - 1) / kRouterMfmaTokens) *
-                      ((E + router_tile_experts(E) - 1) / router_tile_experts(E));
+                      ((Er + router_tile_experts(Er) - 1) / router_tile_experts(Er));
     p->router_split = largest_divisor_at_most(c.d_model / kRouterMfmaK, std::max(1, (512 + tiles - 1) / tiles));
   }
   // GEMM row tiles: sum_e ceil(c_e / rows) <= ceil(R / rows) + (non-empty experts)
@@ -147,7 +151,7 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   p->ctrl = take(4 * (1 + (size_t)c.d_model / kStreamCols));
   p->ctrl_bytes = off;  // aligned end of the control words (they start at offset 0)
   p->flags = take(4);
-  p->logits = take(sizeof(double) * (size_t)std::max({1, p->router_split, p->small_split}) * T * E);
+  p->logits = take(sizeof(double) * (size_t)std::max({1, p->router_split, p->small_split}) * T * Er);
   p->topk_idx = take(4 * R);
   p->topk_w = take(4 * R);
   p->counts = take(4 * (size_t)E);
@@ -188,7 +192,7 @@ moe_status check_forward_args(moe_handle h, int32_t T, const uint16_t* hidden, c
   moe_status st = check_handle(h);
   if (st != MOE_OK) return st;
   if ((st = check_T(h, T)) != MOE_OK) return st;
-  moe::make_plan(h->cfg, T, plan);
+  moe::make_plan(h->ecfg, T, plan);
   if (T == 0) return MOE_OK;
   if (!hidden || !router_w || !slot_table || !w || !out || !workspace)
     return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
@@ -222,16 +226,17 @@ moe_status enqueue(moe_layer* h, const moe::Plan& p, const uint16_t* hidden, con
   };
   // with few tokens the regroup runs inside the router kernel and the
   // combine inside the down kernel (their stages then time as empty)
+  const moe_config& c = h->ecfg;
   mark(0);
-  moe::launch_router(h->cfg, p, hidden, router_w, router_bias, slot_table, ws, s);
+  moe::launch_router(c, p, hidden, router_w, router_bias, slot_table, ws, s);
   mark(1);
-  if (!p.fused_small) moe::launch_permute(h->cfg, p, slot_table, ws, s);
+  if (!p.fused_small) moe::launch_permute(c, p, slot_table, ws, s);
   mark(2);
-  moe::launch_gateup(h->cfg, p, hidden, *w, ws, s);
+  moe::launch_gateup(c, p, hidden, *w, ws, s);
   mark(3);
-  moe::launch_down(h->cfg, p, *w, out, ws, s);
+  moe::launch_down(c, p, *w, out, ws, s);
   mark(4);
-  if (!p.fused_small) moe::launch_combine(h->cfg, p, out, ws, s);
+  if (!p.fused_small) moe::launch_combine(c, p, out, ws, s);
   mark(5);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
@@ -269,9 +274,15 @@ MOE_EXPORT moe_status moe_create(const moe_config* cfg, moe_handle* out) {
   if (c.num_slots < 1) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "num_slots=%d must be >= 1", c.num_slots);
   if (c.max_tokens < 1 || c.max_tokens > 65536)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "max_tokens=%d outside [1, 65536]", c.max_tokens);
+  if (c.num_shared < 0 || c.top_k + c.num_shared > 8 || c.num_experts + c.num_shared > 256)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "num_shared=%d: need >= 0, top_k + num_shared <= 8 and "
+                "num_experts + num_shared <= 256", c.num_shared);
   moe_layer* h = new (std::nothrow) moe_layer;
   if (!h) return fail(MOE_ERR_INVALID_ARG, "out of host memory");
   h->cfg = c;
+  h->ecfg = c;
+  h->ecfg.num_experts = c.num_experts + c.num_shared;
+  h->ecfg.top_k = c.top_k + c.num_shared;
   *out = h;
   return MOE_OK;
 }
@@ -289,7 +300,7 @@ MOE_EXPORT moe_status moe_control_bytes(moe_handle h, size_t* bytes) {
   if (st != MOE_OK) return st;
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
   moe::Plan p;
-  moe::make_plan(h->cfg, 0, &p);
+  moe::make_plan(h->ecfg, 0, &p);
   *bytes = p.ctrl_bytes;
   return MOE_OK;
 }
@@ -300,7 +311,7 @@ MOE_EXPORT moe_status moe_workspace_size(moe_handle h, int32_t T, size_t* bytes)
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
   if ((st = check_T(h, T)) != MOE_OK) return st;
   moe::Plan p;
-  moe::make_plan(h->cfg, T, &p);
+  moe::make_plan(h->ecfg, T, &p);
   *bytes = p.total;
   return MOE_OK;
 }
@@ -322,7 +333,7 @@ MOE_EXPORT moe_status moe_routing_view(moe_handle h, const void* workspace, int3
   if (!workspace || !view) return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
   if ((st = check_T(h, T)) != MOE_OK) return st;
   moe::Plan p;
-  moe::make_plan(h->cfg, T, &p);
+  moe::make_plan(h->ecfg, T, &p);
   const char* ws = static_cast<const char*>(workspace);
   view->topk_idx = reinterpret_cast<const int32_t*>(ws + p.topk_idx);
   view->topk_w = reinterpret_cast<const float*>(ws + p.topk_w);
@@ -382,7 +393,7 @@ MOE_EXPORT moe_status moe_device_flags(moe_handle h, const void* workspace, int3
   if (!workspace || !flags) return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
   if ((st = check_T(h, T)) != MOE_OK) return st;
   moe::Plan p;
-  moe::make_plan(h->cfg, T, &p);
+  moe::make_plan(h->ecfg, T, &p);
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t v = 0;
   hipError_t err = hipMemcpyAsync(&v, static_cast<const char*>(workspace) + p.flags, sizeof v,

@@ -17,14 +17,17 @@ constexpr int kFusedLogitsLds = 4096;  // logits (T x E) the fused router's last
 // Top-k of one token, run by one wave: add the bias to the (split-summed)
 // logits, then k rounds of a wave-wide arg-max over the experts not yet
 // chosen (largest logit, ties to the lower id), then
-// w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+// w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).  Token t's row of topk_idx /
+// topk_w has kt = k + ns columns: the k routed experts, then the ns shared
+// experts E .. E+ns-1 with weight 1.
 // kCoherent: read the logits with device-scope coherent loads (they were
 // written by other blocks of the same kernel); otherwise plain loads, summing
 // nsplit k-split partials.
 template <bool kCoherent>
 __device__ void topk_token(const double* __restrict__ logits, int nsplit, const float* __restrict__ bias, int T,
-                           int E, int k, int t, int lane, int32_t* __restrict__ topk_idx,
+                           int E, int k, int ns, int t, int lane, int32_t* __restrict__ topk_idx,
                            float* __restrict__ topk_w) {
+  const int kt = k + ns;
   constexpr int kPer = 4;  // experts per lane: E <= 256
   double l[kPer];
   bool live[kPer];
@@ -81,8 +84,12 @@ __device__ void topk_token(const double* __restrict__ logits, int nsplit, const 
       den += ex[j];
     }
     for (int j = 0; j < k; ++j) {
-      topk_idx[(size_t)t * k + j] = bid[j];
-      topk_w[(size_t)t * k + j] = (float)(ex[j] / den);
+      topk_idx[(size_t)t * kt + j] = bid[j];
+      topk_w[(size_t)t * kt + j] = (float)(ex[j] / den);
+    }
+    for (int j = 0; j < ns; ++j) {
+      topk_idx[(size_t)t * kt + k + j] = E + j;
+      topk_w[(size_t)t * kt + k + j] = 1.0f;
     }
   }
 }
@@ -93,12 +100,14 @@ __device__ void topk_token(const double* __restrict__ logits, int nsplit, const 
 // butterfly over the lanes and a fixed-order sum over the 4 waves (through
 // LDS) finish each logit.  The last block to finish (an atomic ticket in the
 // workspace's control words) then runs the top-k of every token and the
-// regroup, and clears the ticket for the next call.
+// regroup, and clears the ticket for the next call.  E and k count the routed
+// experts; the ns shared experts (groups E .. E+ns-1 of the regroup, ra.E =
+// E + ns) take the last ns columns of every token.
 __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ hidden,
                                                            const float* __restrict__ wr,
                                                            const float* __restrict__ bias,
                                                            double* __restrict__ logits, int T, int d, int E,
-                                                           int k, int32_t* __restrict__ topk_idx,
+                                                           int k, int ns, int32_t* __restrict__ topk_idx,
                                                            float* __restrict__ topk_w,
                                                            uint32_t* __restrict__ flags,
                                                            uint32_t* __restrict__ ticket, RegroupArgs ra) {
@@ -164,8 +173,8 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
     for (int i0 = 0; i0 < TE; i0 += 4 * 256) {
       float bv = 0.0f;
       int sl = 0;
-      if (i0 == 0 && threadIdx.x < E) {
-        bv = bias ? bias[threadIdx.x] : 0.0f;
+      if (i0 == 0 && threadIdx.x < ra.E) {  // slots of routed and shared experts, bias of routed ones
+        bv = (bias && threadIdx.x < E) ? bias[threadIdx.x] : 0.0f;
         sl = ra.slot_table[threadIdx.x];
       }
       // logit = split 0 + split 1 + ... in order; up to kRouterSmallMaxSplit
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int sp = 1; sp < kRouterSmallMaxSplit; ++sp) v[u] += sp < nsplit ? w[u][sp - 1] : 0.0;
-      if (i0 == 0 && threadIdx.x < E) {
+      if (i0 == 0 && threadIdx.x < ra.E) {
         sbias[threadIdx.x] = bv;
         sslot[threadIdx.x] = sl;
       }
@@ -243,12 +252,17 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
           ex[r] = r < k ? expf((float)(val[r] - val[0])) : 0.0f;
           den += ex[r];
         }
+        const int kt = k + ns;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           if (r < k) {
-            topk_idx[(size_t)t * k + r] = cid[r];
-            topk_w[(size_t)t * k + r] = ex[r] / den;
-            sid[t * k + r] = cid[r];
+            topk_idx[(size_t)t * kt + r] = cid[r];
+            topk_w[(size_t)t * kt + r] = ex[r] / den;
+            sid[t * kt + r] = cid[r];
+          } else if (r < kt) {  // shared experts
+            topk_idx[(size_t)t * kt + r] = E + r - k;
+            topk_w[(size_t)t * kt + r] = 1.0f;
+            sid[t * kt + r] = E + r - k;
           }
         }
       }
@@ -261,7 +275,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
     if (threadIdx.x == 0) reset_ticket(ticket);
     return;
   }
-  for (int t = wave; t < T; t += 4) topk_token<true>(logits, nsplit, bias, T, E, k, t, lane, topk_idx, topk_w);
+  for (int t = wave; t < T; t += 4) topk_token<true>(logits, nsplit, bias, T, E, k, ns, t, lane, topk_idx, topk_w);
   __syncthreads();
   regroup_block<256>(ra);
   if (threadIdx.x == 0) reset_ticket(ticket);
@@ -350,14 +364,14 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t*
 __global__ __launch_bounds__(256) void router_topk_kernel(const double* __restrict__ logits, int nsplit,
                                                           const float* __restrict__ bias,
                                                           const uint16_t* __restrict__ hidden, int d, int T,
-                                                          int E, int k, int32_t* __restrict__ topk_idx,
+                                                          int E, int k, int ns, int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ topk_w, float* __restrict__ xsum,
                                                           uint16_t* __restrict__ xperm, uint32_t* __restrict__ flags) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
-  topk_token<false>(logits, nsplit, bias, T, E, k, t, lane, topk_idx, topk_w);
+  topk_token<false>(logits, nsplit, bias, T, E, k, ns, t, lane, topk_idx, topk_w);
   // row sum of x (for the gate/up GEMM's zero-point term) and x in fragment
   // k-order (the gate/up GEMM's A operand then needs no permutes)
   double sx = 0.0;
@@ -376,29 +390,31 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const double* __restri
 
 void launch_router(const moe_config& c, const Plan& p, const uint16_t* hidden, const float* router_w,
                    const float* router_bias, const int32_t* slot_table, char* ws, hipStream_t s) {
+  // c counts shared experts among the experts and the columns of each token;
+  // the router itself sees the routed ones only
+  const int ns = c.num_shared, E = c.num_experts - ns, k = c.top_k - ns;
   double* logits = reinterpret_cast<double*>(ws + p.logits);
   int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + p.topk_idx);
   float* topk_w = reinterpret_cast<float*>(ws + p.topk_w);
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws + p.flags);
   if (p.fused_small) {
-    dim3 grid(c.num_experts, (p.T + kRouterTokTile - 1) / kRouterTokTile, p.small_split);
-    router_small_kernel<<<grid, 256, 0, s>>>(hidden, router_w, router_bias, logits, p.T, c.d_model,
-                                             c.num_experts, c.top_k, topk_idx, topk_w, flags,
-                                             reinterpret_cast<uint32_t*>(ws + p.ctrl),
+    dim3 grid(E, (p.T + kRouterTokTile - 1) / kRouterTokTile, p.small_split);
+    router_small_kernel<<<grid, 256, 0, s>>>(hidden, router_w, router_bias, logits, p.T, c.d_model, E, k, ns,
+                                             topk_idx, topk_w, flags, reinterpret_cast<uint32_t*>(ws + p.ctrl),
                                              regroup_args(c, p, slot_table, ws));
     return;
   }
-  const int tn = router_tile_experts(c.num_experts);
-  dim3 grid((p.T + kRouterMfmaTokens - 1) / kRouterMfmaTokens, (c.num_experts + tn - 1) / tn, p.router_split);
+  const int tn = router_tile_experts(E);
+  dim3 grid((p.T + kRouterMfmaTokens - 1) / kRouterMfmaTokens, (E + tn - 1) / tn, p.router_split);
   const int kchunk = c.d_model / p.router_split;
   if (tn == 64)
-    router_logits_mfma_kernel<64><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, c.num_experts, kchunk);
+    router_logits_mfma_kernel<64><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, E, kchunk);
   else if (tn == 32)
-    router_logits_mfma_kernel<32><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, c.num_experts, kchunk);
+    router_logits_mfma_kernel<32><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, E, kchunk);
   else
-    router_logits_mfma_kernel<16><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, c.num_experts, kchunk);
+    router_logits_mfma_kernel<16><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, E, kchunk);
   router_topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(logits, p.router_split, router_bias, hidden, c.d_model, p.T,
-                                                   c.num_experts, c.top_k, topk_idx, topk_w,
+                                                   E, k, ns, topk_idx, topk_w,
                                                    reinterpret_cast<float*>(ws + p.xsum),
                                                    reinterpret_cast<uint16_t*>(ws + p.xperm), flags);
 }

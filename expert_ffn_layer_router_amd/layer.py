@@ -51,9 +51,9 @@ class MoeLayer:
     moe_graph_capture / moe_graph_launch / moe_device_flags."""
 
     def __init__(self, d_model: int, d_ff: int, num_experts: int, top_k: int, num_slots: int,
-                 max_tokens: int):
+                 max_tokens: int, num_shared: int = 0):
         self.lib = _lib.load()
-        self.cfg = _lib.MoeConfig(d_model, d_ff, num_experts, top_k, num_slots, max_tokens, 0)
+        self.cfg = _lib.MoeConfig(d_model, d_ff, num_experts, top_k, num_slots, max_tokens, 0, num_shared)
         h = ctypes.c_void_p()
         _lib.check(self.lib.moe_create(ctypes.byref(self.cfg), ctypes.byref(h)))
         self.handle = h
@@ -127,7 +127,10 @@ class MoeLayer:
         v = _lib.MoeRouting()
         _lib.check(self.lib.moe_routing_view(self.handle, _ptr(workspace), int(T), ctypes.byref(v)))
         base = int(workspace.data_ptr())
-        k, E, R = self.cfg.top_k, self.cfg.num_experts, int(T) * self.cfg.top_k
+        # shared experts are extra columns of every token and extra groups
+        k = self.cfg.top_k + self.cfg.num_shared
+        E = self.cfg.num_experts + self.cfg.num_shared
+        R = int(T) * k
 
         def view(ptr, n, dtype):
             off = int(ptr) - base

@@ -6,6 +6,8 @@
  *     FFN_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x)),
  * with the expert weights stored as per-row int4 codes plus an fp16 scale and
  * zero-point (W = (q - z) * s) and read through an expert-to-slot table.
+ * Optional shared experts are added for every token with weight 1:
+ *     out[t] += sum over s < num_shared of FFN_{E+s}(x[t]).
  *
  * Where each step comes from (three web pages on expert offloading for MoE
  * inference; the "Strata" page is titled "125B MoE at 100+ tok/s on an
@@ -19,6 +21,8 @@
  *                 experts' contiguous token groups)
  *   slots         Co-inference page, section 2.2 (experts held in GPU cache
  *                 slots); Strata page, section 2.1 (hot-expert pool)
+ *   shared expert Strata page, section 2.1 (the shared expert of MoE models,
+ *                 kept resident with the layers every token uses)
  *   graph replay  Strata page, section 3.4 (the decode step captured once and
  *                 replayed, with a fixed batch and buffers allocated first)
  *
@@ -58,17 +62,21 @@ typedef enum moe_status {
 } moe_status;
 
 /* Device error bits, reported by moe_device_flags. */
-#define MOE_FLAG_BAD_SLOT 0x1u      /* slot_table[e] outside [0, num_slots) for a routed expert;
+#define MOE_FLAG_BAD_SLOT 0x1u      /* slot_table[e] outside [0, num_slots) for an expert with rows;
                                        that expert contributed zero */
 
 typedef struct moe_config {
   int32_t d_model;      /* hidden width d; multiple of 128 */
   int32_t d_ff;         /* expert inner width; multiple of 128 */
-  int32_t num_experts;  /* E, 1..256 */
-  int32_t top_k;        /* k, 1..min(E, 8) */
+  int32_t num_experts;  /* E, routed experts (rows of the router), 1..256 */
+  int32_t top_k;        /* k, routed experts per token, 1..min(E, 8) */
   int32_t num_slots;    /* slots in the weight pool, >= 1 */
   int32_t max_tokens;   /* largest T a call may pass, 1..65536 */
   uint32_t flags;       /* reserved, must be 0 */
+  int32_t num_shared;   /* shared experts, 0 <= S with k + S <= 8 and E + S <= 256.  Shared
+                           expert s has id E + s and the shape of a routed expert; every
+                           token takes it with weight exactly 1, after its k routed ones.
+                           Its weights are in pool slot slot_table[E + s]. */
 } moe_config;
 
 /* Per-slot weight pool (device pointers, caller-owned).  Slot s of a matrix
@@ -84,13 +92,16 @@ typedef struct moe_weights {
   const uint16_t *s_down, *z_down;  /* [num_slots][d_model] */
 } moe_weights;
 
-/* Device pointers into a workspace after a forward with T tokens (R = T*k). */
+/* Device pointers into a workspace after a forward with T tokens.  With S
+ * shared experts every token has K = k + S columns (R = T*K rows, E + S
+ * groups): columns 0..k-1 are its routed experts, column k + s is shared
+ * expert E + s with weight 1, so each shared group holds all T tokens. */
 typedef struct moe_routing {
-  const int32_t *topk_idx;  /* [T][k]  chosen experts, logit descending, ties to lower id */
-  const float *topk_w;      /* [T][k]  softmax over the k chosen logits */
-  const int32_t *counts;    /* [E]     rows per expert */
-  const int32_t *offsets;   /* [E+1]   exclusive prefix sum of counts */
-  const int32_t *perm;      /* [R]     grouped position p -> assignment a = t*k + j */
+  const int32_t *topk_idx;  /* [T][K]  routed: logit descending, ties to lower id; then E..E+S-1 */
+  const float *topk_w;      /* [T][K]  softmax over the k chosen logits; 1 for shared columns */
+  const int32_t *counts;    /* [E+S]   rows per expert */
+  const int32_t *offsets;   /* [E+S+1] exclusive prefix sum of counts */
+  const int32_t *perm;      /* [R]     grouped position p -> assignment a = t*K + j */
   const int32_t *inv_perm;  /* [R]     assignment a -> grouped position p */
 } moe_routing;
 
@@ -100,7 +111,8 @@ typedef void *moe_stream; /* a hipStream_t */
 /* Creates a handle for one layer shape.  Host only: no device call, no device
  * allocation.  Returns MOE_ERR_UNSUPPORTED_SHAPE for shapes outside:
  * d_model % 128 == 0, d_ff % 128 == 0, 1 <= E <= 256, 1 <= k <= min(E, 8),
- * num_slots >= 1, 1 <= max_tokens <= 65536, flags == 0. */
+ * num_slots >= 1, 1 <= max_tokens <= 65536, flags == 0, num_shared >= 0,
+ * k + num_shared <= 8, E + num_shared <= 256. */
 moe_status moe_create(const moe_config *cfg, moe_handle *out);
 
 /* Frees the handle and any captured graph.  NULL is ignored. */
@@ -119,7 +131,7 @@ moe_status moe_control_bytes(moe_handle h, size_t *bytes);
  *   hidden       bf16 [T][d_model]
  *   router_w     fp32 [E][d_model]
  *   router_bias  fp32 [E], or NULL for none
- *   slot_table   int32 [E], device memory, read when the kernels run
+ *   slot_table   int32 [E + num_shared], device memory, read when the kernels run
  *   w            the slot-indexed weight pool
  *   out          bf16 [T][d_model]
  *   workspace    at least moe_workspace_size(T) bytes, zero-filled before its

@@ -46,12 +46,40 @@ def test_status_strings(lib):
 @pytest.mark.parametrize("kw", [dict(d_model=100), dict(d_model=0), dict(d_ff=200), dict(num_experts=0),
                                 dict(num_experts=257), dict(top_k=0), dict(top_k=9, num_experts=16),
                                 dict(top_k=9, num_experts=9), dict(top_k=3, num_experts=2),
-                                dict(num_slots=0), dict(max_tokens=0), dict(max_tokens=65537), dict(flags=1)])
+                                dict(num_slots=0), dict(max_tokens=0), dict(max_tokens=65537), dict(flags=1),
+                                dict(num_shared=-1), dict(top_k=2, num_shared=7),
+                                dict(num_experts=256, top_k=1, num_shared=1)])
 def test_create_rejects_unsupported_shapes(lib, kw):
     st, h = _create(lib, **kw)
     assert st == _lib.MOE_ERR_UNSUPPORTED_SHAPE, _lib.last_error()
     assert not h.value
     assert _lib.last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(top_k=2, num_shared=6), dict(num_experts=255, top_k=1, num_shared=1),
+                                dict(num_experts=1, top_k=1, num_shared=7)])
+def test_create_accepts_shared_expert_limits(lib, kw):
+    st, h = _create(lib, **kw)
+    assert st == 0, _lib.last_error()
+    lib.moe_destroy(h)
+
+
+def test_shared_experts_add_rows_to_the_workspace(lib):
+    """With S shared experts every token has k + S rows: the workspace grows like
+    a layer with top_k + S, beyond the routed-only one."""
+    sizes = {}
+    for k, S in ((2, 0), (2, 2), (4, 0)):
+        st, h = _create(lib, top_k=k, num_shared=S, num_experts=8, max_tokens=4096)
+        assert st == 0
+        n = ctypes.c_size_t()
+        for T in (16, 4096):
+            assert lib.moe_workspace_size(h, T, ctypes.byref(n)) == 0
+            sizes[(k, S, T)] = n.value
+        lib.moe_destroy(h)
+    for T in (16, 4096):
+        assert sizes[(2, 0, T)] < sizes[(2, 2, T)]
+        # same rows as top-4, at most the few bytes of two more groups' counters apart
+        assert abs(sizes[(2, 2, T)] - sizes[(4, 0, T)]) <= 2048
 
 
 def test_create_null_arguments(lib):

@@ -42,11 +42,12 @@ def _oracle(case, hidden=None, **over):
     kw.update(over)
     prec = "f64" if case.shape.d_model * case.shape.d_ff <= 128 * 256 else "f32"
     return oracle.forward(case.hidden if hidden is None else hidden, top_k=case.shape.top_k, precision=prec,
-                          **kw)
+                          num_shared=case.shape.num_shared, **kw)
 
 
 @pytest.mark.parametrize("name", ["tiny", "fine_tiny", "mixtral_decode", "phi35_skew", "fine_decode",
-                                  "mixtral_prefill", "fine_prefill"])
+                                  "mixtral_prefill", "fine_prefill", "shared_tiny", "fine_shared_tiny",
+                                  "shared_decode", "shared_prefill"])
 def test_layer_parity(name):
     require_gpu()
     say(f"{name}: generating layer")
@@ -63,7 +64,9 @@ def test_layer_parity(name):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 3), ("tiny", 37), ("fine_tiny", 100),
-                                    ("fine_tiny", 257), ("tiny", 1000)])
+                                    ("fine_tiny", 257), ("tiny", 1000), ("shared_tiny", 1),
+                                    ("shared_tiny", 33), ("shared_tiny", 300), ("fine_shared_tiny", 64),
+                                    ("fine_shared_tiny", 65)])
 def test_ragged_token_counts(name, T):
     require_gpu()
     case = synth.make_case(name, T=T)
@@ -88,20 +91,21 @@ def test_zero_router_ties_go_to_lowest_ids():
     assert_out_close(res["out"], ref["out"])
 
 
-@pytest.mark.parametrize("E,k", [(1, 1), (4, 4), (8, 1), (16, 8), (256, 8)])
-def test_small_special_shapes(E, k):
+@pytest.mark.parametrize("E,k,S", [(1, 1, 0), (4, 4, 0), (8, 1, 0), (16, 8, 0), (256, 8, 0), (1, 1, 1),
+                                   (8, 6, 2), (255, 1, 1), (4, 1, 7)])
+def test_small_special_shapes(E, k, S):
     require_gpu()
-    shape = synth.LayerShape(24, 128, 256, E, k, E, "identity", 0.0)
+    shape = synth.LayerShape(24, 128, 256, E, k, E + S, "identity", 0.0, S)
     w = synth.make_weights(shape, seed=3)
     x = synth.make_hidden(24, 128, seed=3)
     case = synth.Case("special", shape, 3, x, w)
-    say(f"special E={E} k={k}")
+    say(f"special E={E} k={k} shared={S}")
     res = GpuLayer(shape, w).run(x)
     ref = _oracle(case)
     check_routing(res, ref)
     assert_out_close(res["out"], ref["out"])
     if k == E:
-        assert np.all(np.sort(res["topk_idx"], axis=1) == np.arange(E))
+        assert np.all(np.sort(res["topk_idx"], axis=1) == np.arange(E + S))
 
 
 @pytest.mark.parametrize("T", [16, 300])
@@ -118,6 +122,23 @@ def test_out_of_range_slot_sets_flag_and_contributes_zero(T):
     assert_out_close(res["out"], ref["out"])
     clean = gpu_layer(case).run(case.hidden)
     assert clean["flags"] == 0                    # each forward clears the flags
+
+
+@pytest.mark.parametrize("T", [16, 300])
+def test_out_of_range_shared_slot_sets_flag_and_contributes_zero(T):
+    require_gpu()
+    case = synth.make_case("shared_tiny", T=T)
+    table = case.weights.slot_table.copy()
+    table[case.shape.num_experts] = -1            # the shared expert's slot
+    say(f"shared_tiny: bad shared slot, T={T}")
+    res = gpu_layer(case).run(case.hidden, slot_table=table)
+    assert res["flags"] & 1
+    ref = _oracle(case, slot_table=table)
+    check_routing(res, ref)
+    assert_out_close(res["out"], ref["out"])
+    routed_only = oracle.forward(case.hidden, top_k=1, precision="f64",
+                                 **dict(weights_kwargs(case.weights), slot_table=table[:-1]))["out"]
+    np.testing.assert_allclose(ref["out"], routed_only, rtol=0, atol=0)
 
 
 def test_deterministic_and_slot_permutation_invariant():
