@@ -10,7 +10,9 @@ route evaluates faster):
 
     out[t] = sum over the k selected experts e of w[t,e] * FFN_e(x[t])
     FFN_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x)),   silu(z) = z / (1 + exp(-z))
-    W_hat    = (q - z) * s       per output row, codes q in [0, 15]
+    W_hat    = (q - z) * s       per output row (or per output row and group of
+                                 128 inputs), codes q in [0, 15] (int4) or
+                                 [0, 255] (8-bit)
 
 with the weights of expert e read from pool slot slot_table[e].  Shared
 experts E .. E + S - 1 (if any) are added for every token with weight 1:
@@ -27,7 +29,8 @@ expert offloading for MoE inference):
       section 3.2 -- the expert FFN is a two-layer MLP, evaluated as a group
                      GEMM over tokens concatenated per expert;
       section 4.2 -- tokens are regrouped by expert id each step.
-  * Co-inference page, section 5.1 -- the router stays in full precision.
+  * Co-inference page, section 5.1 -- the router stays in full precision;
+      8-bit expert weights and grouped quantisation.
   * Mira page, section 4.2 -- Top-K gating.
 
 Readings where the pages are silent (each is listed in the design notes):
@@ -41,7 +44,10 @@ Parity pins (tests marked "not gpu"): hand-worked closed forms, W_r = 0 and
 k = E special cases, brute-force routing and regrouping by pure-Python loops,
 a dense all-experts-then-mask evaluation, a dense SwiGLU via torch's CPU silu,
 codec round trips and error bounds, q == z giving exactly zero, exact
-power-of-two scale laws, slot-permutation invariance and fp32/fp64 agreement.
+power-of-two scale laws, slot-permutation invariance and fp32/fp64 agreement;
+for the other weight formats, hand-worked 8-bit and grouped dequantisation,
+the reductions grouped-with-row-parameters == per-row and 8-bit with 16x the
+int4 codes == int4, and the outlier confinement grouping exists for.
 """
 
 from .numerics import bf16_to_f64, fp16_to_f64  # noqa: F401

@@ -16,7 +16,7 @@ from .routing import route
 
 
 def brute_dense(hidden, router_w, router_b, slot_table, w_gate, w_up, w_down,
-                s_gate, z_gate, s_up, z_up, s_down, z_down, top_k, num_shared=0):
+                s_gate, z_gate, s_up, z_up, s_down, z_down, top_k, num_shared=0, bits=4, group=0):
     x = bf16_to_f64(hidden)
     T, d = x.shape
     E = np.asarray(router_w).shape[0]
@@ -33,10 +33,10 @@ def brute_dense(hidden, router_w, router_b, slot_table, w_gate, w_up, w_down,
         slot = int(slot_table[e])
         if not 0 <= slot < S:
             continue
-        F = expert_ffn(x, slot, dtype=np.float64, **wts)
+        F = expert_ffn(x, slot, dtype=np.float64, bits=bits, group=group, **wts)
         out += mask[:, e:e + 1] * F
     for e in range(E, E + int(num_shared)):   # shared experts: every token, weight 1
         slot = int(slot_table[e])
         if 0 <= slot < S:
-            out += expert_ffn(x, slot, dtype=np.float64, **wts)
+            out += expert_ffn(x, slot, dtype=np.float64, bits=bits, group=group, **wts)
     return out

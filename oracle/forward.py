@@ -40,24 +40,25 @@ def _silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(X, slot, w_gate, w_up, w_down, s_gate, z_gate, s_up, z_up, s_down, z_down, dtype=np.float64):
+def expert_ffn(X, slot, w_gate, w_up, w_down, s_gate, z_gate, s_up, z_up, s_down, z_down, dtype=np.float64,
+               bits=4, group=0):
     """Y = Wd (silu(X Wg^T) * (X Wu^T))^T-rows for the rows X [n, d] of one expert."""
     X = np.asarray(X, dtype=dtype)
-    Wg = dequantize(w_gate[slot], s_gate[slot], z_gate[slot], dtype)
+    Wg = dequantize(w_gate[slot], s_gate[slot], z_gate[slot], dtype, bits, group)
     G = X @ Wg.T
     del Wg
-    Wu = dequantize(w_up[slot], s_up[slot], z_up[slot], dtype)
+    Wu = dequantize(w_up[slot], s_up[slot], z_up[slot], dtype, bits, group)
     U = X @ Wu.T
     del Wu
     H = _silu(G) * U
     del G, U
-    Wd = dequantize(w_down[slot], s_down[slot], z_down[slot], dtype)
+    Wd = dequantize(w_down[slot], s_down[slot], z_down[slot], dtype, bits, group)
     return H @ Wd.T
 
 
 def forward(hidden, router_w, router_b, slot_table, w_gate, w_up, w_down,
             s_gate, z_gate, s_up, z_up, s_down, z_down, top_k, precision="f64", tokens=None,
-            num_shared=0):
+            num_shared=0, bits=4, group=0):
     """Returns a dict with the routing, the regrouping and out (fp64).
 
     tokens: optional sorted array of token indices; out then holds only those
@@ -65,6 +66,8 @@ def forward(hidden, router_w, router_b, slot_table, w_gate, w_up, w_down,
     num_shared: shared experts after the E routed ones; slot_table then has
     E + num_shared entries and topk_idx / topk_w have top_k + num_shared
     columns.
+    bits, group: the weight format (codec.dequantize): 4 or 8-bit codes, one
+    (s, z) per output row (group 0) or per output row and group of K inputs.
     """
     dtype = {"f64": np.float64, "f32": np.float32}[precision]
     hidden = np.asarray(hidden)
@@ -90,6 +93,7 @@ def forward(hidden, router_w, router_b, slot_table, w_gate, w_up, w_down,
     Y = {}  # assignment a -> row of expert output
     wts = dict(w_gate=w_gate, w_up=w_up, w_down=w_down, s_gate=s_gate, z_gate=z_gate,
                s_up=s_up, z_up=z_up, s_down=s_down, z_down=z_down)
+    grp = int(group)
     for e in range(E):
         group = perm[offsets[e]:offsets[e + 1]]          # assignments of expert e, ascending
         group = group[want[group // k]]
@@ -97,7 +101,7 @@ def forward(hidden, router_w, router_b, slot_table, w_gate, w_up, w_down,
             continue
         slot = int(slot_table[e])
         if 0 <= slot < S:
-            Ye = expert_ffn(x[group // k], slot, dtype=dtype, **wts).astype(np.float64)
+            Ye = expert_ffn(x[group // k], slot, dtype=dtype, bits=bits, group=grp, **wts).astype(np.float64)
         else:
             Ye = np.zeros((group.size, d), dtype=np.float64)
         for r, a in enumerate(group):

@@ -17,17 +17,21 @@ in parallel):
     W_down ~ N(0,1)/sqrt(d_ff) of shape [d, d_ff], each encoded to asymmetric
     unsigned int4 with one fp16 scale and one integer zero-point (stored as
     fp16) per output row -- the per-expert quantisation of the Strata page,
-    section 3.1;
+    section 3.1 -- or, for the other weight formats, to 8-bit codes and/or
+    one (s, z) per output row and group of 128 inputs (the 8-bit, grouped
+    quantisation of the Co-inference page, section 5.1);
   * shared experts (num_shared > 0) are drawn like routed experts E, E+1, ...
     and have no router row;
   * the pool has num_slots slots; expert e lives at slot slot_table[e];
     slots no expert uses are filled with random codes and NaN scales so that a
     wrong indirection cannot go unnoticed.
 
-Encoding rule (input preparation, not part of the layer's forward): per row,
-lo = min(min W, 0), hi = max(max W, 0), s = fp16((hi-lo)/15) (1 if that is 0),
-z = clip(rint(-lo/s), 0, 15), q = clip(rint(W/s) + z, 0, 15), all in fp32 with
-round-half-to-even; two codes per byte along K, low nibble = even k.
+Encoding rule (input preparation, not part of the layer's forward): per row
+(or per row and group), lo = min(min W, 0), hi = max(max W, 0),
+s = fp16((hi-lo)/qmax) (1 if that is 0), z = clip(rint(-lo/s), 0, qmax),
+q = clip(rint(W/s) + z, 0, qmax), qmax = 2^bits - 1, all in fp32 with
+round-half-to-even; int4: two codes per byte along K, low nibble = even k;
+grouped parameters are stored group-major, [K/G][N].
 """
 
 from __future__ import annotations
@@ -59,11 +63,13 @@ class LayerShape:
     slot_kind: str = "identity"   # identity | perm (all slots, shuffled) | sparse (E + shared of S slots)
     zipf_s: float = 0.0           # 0: no router bias
     num_shared: int = 0           # shared experts (every token, weight 1), numbered E .. E + num_shared - 1
+    bits: int = 4                 # code width: 4 or 8
+    group: int = 0                # 0: one (s, z) per output row; G: per output row and run of G inputs
 
     def family(self) -> tuple:
         """Everything but T and top_k: layers that differ only in those share weights."""
         return (self.d_model, self.d_ff, self.num_experts, self.num_slots,
-                self.slot_kind, float(self.zipf_s), int(self.num_shared))
+                self.slot_kind, float(self.zipf_s), int(self.num_shared), int(self.bits), int(self.group))
 
 
 CASES = {
@@ -87,6 +93,18 @@ CASES = {
     # experts (8 experts per token), both with scattered slots
     "shared_tiny": LayerShape(16, 128, 256, 8, 1, 12, "sparse", 1.0, 1),
     "fine_shared_tiny": LayerShape(16, 128, 256, 64, 6, 80, "sparse", 1.0, 2),
+    # other weight formats: int4 with (s, z) per output row and group of 128
+    # inputs, and 8-bit codes per row or per group of 128
+    "mixtral_decode_q4g128": LayerShape(16, 4096, 14336, 8, 2, 8, "identity", 0.0, 0, 4, 128),
+    "mixtral_prefill_q4g128": LayerShape(2048, 4096, 14336, 8, 2, 8, "identity", 0.0, 0, 4, 128),
+    "mixtral_decode_q8g128": LayerShape(16, 4096, 14336, 8, 2, 8, "identity", 0.0, 0, 8, 128),
+    "mixtral_prefill_q8g128": LayerShape(2048, 4096, 14336, 8, 2, 8, "identity", 0.0, 0, 8, 128),
+    "phi35_skew_q8": LayerShape(64, 4096, 6400, 16, 2, 16, "perm", 1.2, 0, 8, 0),
+    # tiny widths with several groups along both K (d = 256, d_ff = 384: the
+    # down K is not a multiple of 256)
+    "tiny_q4g128": LayerShape(16, 256, 384, 8, 2, 12, "sparse", 1.0, 0, 4, 128),
+    "tiny_q8": LayerShape(16, 256, 384, 8, 2, 12, "sparse", 1.0, 0, 8, 0),
+    "tiny_q8g128": LayerShape(16, 256, 384, 8, 2, 12, "sparse", 1.0, 1, 8, 128),
 }
 
 
@@ -139,22 +157,32 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     return b.astype(np.uint16)
 
 
-def _encode_rows(W: np.ndarray):
-    """Asymmetric per-row int4 encoding of an fp32 matrix (input preparation)."""
-    lo = np.minimum(W.min(axis=1), np.float32(0))
-    hi = np.maximum(W.max(axis=1), np.float32(0))
-    s16 = ((hi - lo) / np.float32(15)).astype(np.float16)
+def _encode_rows(W: np.ndarray, bits: int = 4, group: int = 0):
+    """Asymmetric per-row (group 0) or per-(row, group) integer encoding of an
+    fp32 matrix (input preparation).  Returns (codes as stored, s bits, z bits),
+    the parameters [N] or [K/group, N]."""
+    N, K = W.shape
+    qmax = np.float32((1 << bits) - 1)
+    G = K if group == 0 else group
+    Wg = W.reshape(N, K // G, G)
+    lo = np.minimum(Wg.min(axis=2), np.float32(0))
+    hi = np.maximum(Wg.max(axis=2), np.float32(0))
+    s16 = ((hi - lo) / qmax).astype(np.float16)
     s16[s16 == 0] = np.float16(1)
     s = s16.astype(np.float32)
-    z = np.clip(np.rint(-lo / s), 0, 15).astype(np.float32)
-    q = W / s[:, None]
+    z = np.clip(np.rint(-lo / s), 0, qmax).astype(np.float32)
+    q = Wg / s[:, :, None]
     np.rint(q, out=q)
-    q += z[:, None]
-    np.clip(q, 0, 15, out=q)
-    q8 = q.astype(np.uint8)
+    q += z[:, :, None]
+    np.clip(q, 0, qmax, out=q)
+    q8 = q.reshape(N, K).astype(np.uint8)
     del q
-    packed = (q8[:, 0::2] | (q8[:, 1::2] << 4)).astype(np.uint8)
-    return packed, s16.view(np.uint16), z.astype(np.float16).view(np.uint16)
+    packed = q8 if bits == 8 else (q8[:, 0::2] | (q8[:, 1::2] << 4)).astype(np.uint8)
+    s16, z16 = s16.T, z.astype(np.float16).T            # [K/G, N]
+    if group == 0:
+        s16, z16 = s16[0], z16[0]
+    return np.ascontiguousarray(packed), np.ascontiguousarray(s16).view(np.uint16), \
+        np.ascontiguousarray(z16).view(np.uint16)
 
 
 def draw_dense_expert(shape: LayerShape, seed: int, e: int):
@@ -166,10 +194,10 @@ def draw_dense_expert(shape: LayerShape, seed: int, e: int):
     return wg, wu, wd
 
 
-def _draw_matrix(seed, tag, e, rows, cols, fan_in):
+def _draw_matrix(seed, tag, e, rows, cols, fan_in, bits=4, group=0):
     W = _rng(seed, tag, e).standard_normal((rows, cols), dtype=np.float32)
     W *= np.float32(1 / np.sqrt(fan_in))
-    return _encode_rows(W)
+    return _encode_rows(W, bits, group)
 
 
 def _workers() -> int:
@@ -185,9 +213,10 @@ def _cache_dir() -> str:
 
 
 def _cache_key(shape: LayerShape, seed: int) -> str:
-    d, f, E, S, kind, zs, ns = shape.family()
+    d, f, E, S, kind, zs, ns, bits, group = shape.family()
     shared = f"_sh{ns}" if ns else ""
-    return f"v{_CACHE_VERSION}_d{d}_f{f}_E{E}{shared}_S{S}_{kind}_z{zs:g}_seed{seed}"
+    fmt = "" if (bits, group) == (4, 0) else f"_b{bits}g{group}"
+    return f"v{_CACHE_VERSION}_d{d}_f{f}_E{E}{shared}_S{S}_{kind}_z{zs:g}{fmt}_seed{seed}"
 
 
 def _load_cached(key: str) -> Optional[Weights]:
@@ -242,12 +271,17 @@ def _generate_weights(shape: LayerShape, seed: int) -> Weights:
     else:
         raise ValueError(f"unknown slot_kind {shape.slot_kind!r}")
 
-    w_gate = np.empty((S, f, d // 2), np.uint8)
-    w_up = np.empty((S, f, d // 2), np.uint8)
-    w_down = np.empty((S, d, f // 2), np.uint8)
-    s_gate = np.empty((S, f), np.uint16); z_gate = np.empty((S, f), np.uint16)
-    s_up = np.empty((S, f), np.uint16); z_up = np.empty((S, f), np.uint16)
-    s_down = np.empty((S, d), np.uint16); z_down = np.empty((S, d), np.uint16)
+    bits, group = shape.bits, shape.group
+    if bits not in (4, 8) or group < 0 or (group and (d % group or f % group)):
+        raise ValueError("bits must be 4 or 8 and the group size must divide d_model and d_ff")
+    w_gate = np.empty((S, f, d * bits // 8), np.uint8)
+    w_up = np.empty((S, f, d * bits // 8), np.uint8)
+    w_down = np.empty((S, d, f * bits // 8), np.uint8)
+    gu_p = (S, f) if group == 0 else (S, d // group, f)      # scale / zero-point shapes
+    dn_p = (S, d) if group == 0 else (S, f // group, d)
+    s_gate = np.empty(gu_p, np.uint16); z_gate = np.empty(gu_p, np.uint16)
+    s_up = np.empty(gu_p, np.uint16); z_up = np.empty(gu_p, np.uint16)
+    s_down = np.empty(dn_p, np.uint16); z_down = np.empty(dn_p, np.uint16)
 
     jobs = []
     for e in range(E):
@@ -258,7 +292,7 @@ def _generate_weights(shape: LayerShape, seed: int) -> Weights:
 
     def run(job):
         tag, e, rows, cols, fan_in, (wq, ws, wz), sl = job
-        p, s, z = _draw_matrix(seed, tag, e, rows, cols, fan_in)
+        p, s, z = _draw_matrix(seed, tag, e, rows, cols, fan_in, bits, group)
         wq[sl], ws[sl], wz[sl] = p, s, z
 
     with ThreadPoolExecutor(_workers()) as ex:
@@ -272,7 +306,7 @@ def _generate_weights(shape: LayerShape, seed: int) -> Weights:
         for wq, ws, wz in ((w_gate, s_gate, z_gate), (w_up, s_up, z_up), (w_down, s_down, z_down)):
             wq[sl] = r.integers(0, 256, size=wq.shape[1:], dtype=np.uint8)
             ws[sl] = _FP16_NAN
-            wz[sl] = r.integers(0, 16, size=wz.shape[1:]).astype(np.float16).view(np.uint16)
+            wz[sl] = r.integers(0, 1 << bits, size=wz.shape[1:]).astype(np.float16).view(np.uint16)
 
     return Weights(router_w=router_w, router_b=router_b, slot_table=slot_table,
                    w_gate=w_gate, w_up=w_up, w_down=w_down, s_gate=s_gate, z_gate=z_gate,
@@ -281,7 +315,7 @@ def _generate_weights(shape: LayerShape, seed: int) -> Weights:
 
 @lru_cache(maxsize=2)
 def _weights_memo(family: tuple, top_k: int, seed: int) -> Weights:
-    shape = LayerShape(0, family[0], family[1], family[2], top_k, family[3], family[4], family[5], family[6])
+    shape = LayerShape(0, family[0], family[1], family[2], top_k, family[3], *family[4:])
     big = shape.num_slots * 3 * shape.d_model * shape.d_ff // 2 > (64 << 20)
     key = _cache_key(shape, seed)
     if big:

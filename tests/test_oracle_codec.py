@@ -93,3 +93,103 @@ def test_generator_codes_follow_the_encoding_rule(name):
             np.testing.assert_array_equal(p2, packed[slot])
             np.testing.assert_array_equal(s2, s[slot])
             np.testing.assert_array_equal(z2, z[slot])
+
+
+# ---- 8-bit codes and grouped (s, z) (Co-inference page, section 5.1) ----
+
+def _f16bits(vals):
+    return np.array(vals, np.float16).view(np.uint16)
+
+
+def test_8bit_dequantize_closed_form():
+    # s = 0.5, z = 128: q = 255 -> 63.5, 128 -> 0, 0 -> -64, 129 -> 0.5
+    q = np.array([[255, 128, 0, 129]], np.uint8)
+    assert oracle.pack_codes(q, 8).tolist() == q.tolist()          # one code per byte
+    W = oracle.dequantize(q, _f16bits([0.5]), _f16bits([128]), bits=8)
+    assert W.tolist() == [[63.5, 0.0, -64.0, 0.5]]
+
+
+def test_grouped_dequantize_closed_form_and_layout():
+    """K = 4 in groups of 2; parameters are [K/G][N] (group-major)."""
+    q = np.array([[9, 7, 4, 2],
+                  [8, 8, 15, 0]], np.uint8)
+    # row 0: group 0 (s=1, z=8), group 1 (s=0.5, z=0); row 1: group 0 (s=2, z=8), group 1 (s=0.25, z=15)
+    s = _f16bits([[1.0, 2.0], [0.5, 0.25]])
+    z = _f16bits([[8, 8], [0, 15]])
+    W = oracle.dequantize(oracle.pack_codes(q), s, z, group=2)
+    assert W.tolist() == [[1.0, -1.0, 2.0, 1.0], [0.0, 0.0, 0.0, -3.75]]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_groups_sharing_the_row_parameters_equal_the_per_row_format(bits):
+    rng = np.random.default_rng(5)
+    N, K, G = 6, 512, 128
+    q = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+    s = rng.uniform(0.01, 1, size=N).astype(np.float16).view(np.uint16)
+    z = rng.integers(0, 1 << bits, size=N).astype(np.float16).view(np.uint16)
+    row = oracle.dequantize(oracle.pack_codes(q, bits), s, z, bits=bits)
+    grp = oracle.dequantize(oracle.pack_codes(q, bits), np.tile(s, (K // G, 1)), np.tile(z, (K // G, 1)),
+                            bits=bits, group=G)
+    np.testing.assert_array_equal(grp, row)
+
+
+def test_8bit_codes_16x_the_int4_codes_dequantise_identically():
+    """q8 = 16 q4, z8 = 16 z4, s8 = s4 / 16 describe the same weights exactly."""
+    rng = np.random.default_rng(6)
+    q4 = rng.integers(0, 16, size=(5, 256), dtype=np.uint8)
+    s4 = (2.0 ** rng.integers(-8, 0, size=5)).astype(np.float16)
+    z4 = rng.integers(0, 16, size=5).astype(np.float16)
+    W4 = oracle.dequantize(oracle.pack_codes(q4), s4.view(np.uint16), z4.view(np.uint16))
+    W8 = oracle.dequantize(16 * q4, (s4 / 16).view(np.uint16), (z4 * 16).view(np.uint16), bits=8)
+    np.testing.assert_array_equal(W8, W4)
+
+
+@pytest.mark.parametrize("bits,group", [(8, 0), (4, 128), (8, 128)])
+def test_quantize_error_bound_and_roundtrip_other_formats(bits, group):
+    rng = np.random.default_rng(7)
+    W = (rng.standard_normal((12, 384)) / 16).astype(np.float32)
+    W[3] = 0.0
+    W[4] = np.abs(W[4])
+    packed, s_bits, z_bits = oracle.quantize(W, bits, group)
+    qmax = (1 << bits) - 1
+    q = oracle.unpack_codes(packed, bits)
+    assert q.shape == W.shape and q.max() <= qmax
+    pshape = (W.shape[0],) if group == 0 else (W.shape[1] // group, W.shape[0])
+    assert s_bits.shape == pshape and z_bits.shape == pshape
+    z = z_bits.view(np.float16).astype(np.float64)
+    assert np.all(z == np.rint(z)) and z.min() >= 0 and z.max() <= qmax
+    Wh = oracle.dequantize(packed, s_bits, z_bits, bits=bits, group=group)
+    s = s_bits.view(np.float16).astype(np.float64)
+    s_el = s[:, None] if group == 0 else np.repeat(s.T, group, axis=1)
+    assert np.all(np.abs(W - Wh) <= 0.51 * s_el)
+    np.testing.assert_array_equal(
+        oracle.encode_with(oracle.dequantize(packed, s_bits, z_bits, np.float32, bits, group), s_bits, z_bits,
+                           bits, group), q)
+
+
+def test_grouping_confines_an_outlier_to_its_group():
+    """The reason the page gives for grouped quantisation: one outlier widens
+    the range of its own group only, so the other groups keep their precision."""
+    rng = np.random.default_rng(8)
+    W = (rng.standard_normal((4, 512)) * 0.02).astype(np.float32)
+    W[:, 5] = 3.0                                    # an outlier in group 0 of every row
+    err = {}
+    for group in (0, 128):
+        packed, s, z = oracle.quantize(W, 4, group)
+        err[group] = np.abs(oracle.dequantize(packed, s, z, group=group) - W)[:, 128:].max()
+    assert err[128] * 10 < err[0]
+
+
+@pytest.mark.parametrize("name", ["tiny_q4g128", "tiny_q8", "tiny_q8g128"])
+def test_generator_codes_follow_the_encoding_rule_other_formats(name):
+    case = synth.make_case(name)
+    w, shp = case.weights, case.shape
+    for e in (0, shp.num_experts - 1):
+        slot = int(w.slot_table[e])
+        for W, packed, s, z in zip(synth.draw_dense_expert(shp, case.seed, e),
+                                   (w.w_gate, w.w_up, w.w_down),
+                                   (w.s_gate, w.s_up, w.s_down), (w.z_gate, w.z_up, w.z_down)):
+            p2, s2, z2 = oracle.quantize(W, shp.bits, shp.group)
+            np.testing.assert_array_equal(p2, packed[slot])
+            np.testing.assert_array_equal(s2, s[slot])
+            np.testing.assert_array_equal(z2, z[slot])

@@ -243,3 +243,46 @@ def test_shared_count_must_match_the_slot_table():
     kw = weights_kwargs(case.weights)
     with pytest.raises(ValueError):
         oracle.forward(case.hidden, top_k=1, **kw)           # slot table has E + 1 entries
+
+
+# ---- other weight formats (8-bit codes, grouped (s, z)) ----
+
+@pytest.mark.parametrize("name", ["tiny_q4g128", "tiny_q8", "tiny_q8g128"])
+def test_format_forward_equals_dense_then_mask(name):
+    case = synth.make_case(name)
+    sh = case.shape
+    kw = weights_kwargs(case.weights)
+    fmt = dict(top_k=sh.top_k, num_shared=sh.num_shared, bits=sh.bits, group=sh.group)
+    res = oracle.forward(case.hidden, **fmt, **kw)
+    dense = oracle.brute_dense(case.hidden, **fmt, **kw)
+    assert_out_close(res["out"], dense, rel=1e-12)
+    r32 = oracle.forward(case.hidden, precision="f32", **fmt, **kw)
+    assert_out_close(r32["out"], res["out"], rel=1e-5)
+
+
+def test_int8_layer_with_16x_codes_equals_the_int4_layer():
+    """q8 = 16 q4, z8 = 16 z4, s8 = s4 / 16 (exact in fp16 at these scales):
+    the same weights, so the same output bit for bit."""
+    case = synth.make_case("tiny")
+    kw = weights_kwargs(case.weights)
+    base = oracle.forward(case.hidden, top_k=2, **kw)["out"]
+    kw8 = dict(kw)
+    for m in ("gate", "up", "down"):
+        kw8["w_" + m] = 16 * oracle.unpack_codes(kw["w_" + m])
+        s = kw["s_" + m].view(np.float16)
+        assert np.all((s / np.float16(16)) * np.float16(16) == s)
+        kw8["s_" + m] = (s / np.float16(16)).view(np.uint16)
+        kw8["z_" + m] = (kw["z_" + m].view(np.float16) * np.float16(16)).view(np.uint16)
+    np.testing.assert_array_equal(oracle.forward(case.hidden, top_k=2, bits=8, **kw8)["out"], base)
+
+
+def test_grouped_layer_with_row_parameters_equals_the_row_layer():
+    case = synth.make_case("tiny")
+    kw = weights_kwargs(case.weights)
+    base = oracle.forward(case.hidden, top_k=2, **kw)["out"]
+    kwg = dict(kw)
+    d, f = case.shape.d_model, case.shape.d_ff
+    for m, K in (("gate", d), ("up", d), ("down", f)):
+        for p in ("s_", "z_"):
+            kwg[p + m] = np.repeat(kw[p + m][:, None, :], K // 128, axis=1)   # [S, K/128, N]
+    np.testing.assert_array_equal(oracle.forward(case.hidden, top_k=2, group=128, **kwg)["out"], base)
