@@ -38,7 +38,9 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
 DECODE_BOUND = {"mixtral_decode": "hbm", "phi35_skew": "hbm", "fine_decode": "hbm", "tiny": "hbm",
                 "fine_tiny": "hbm", "mixtral_prefill": "mfma", "fine_prefill": "mfma",
-                "shared_decode": "hbm", "shared_prefill": "mfma", "shared_tiny": "hbm", "fine_shared_tiny": "hbm"}
+                "shared_decode": "hbm", "shared_prefill": "mfma", "shared_tiny": "hbm", "fine_shared_tiny": "hbm",
+                "mixtral_decode_q4g128": "hbm", "mixtral_decode_q8g128": "hbm", "phi35_skew_q8": "hbm",
+                "mixtral_prefill_q4g128": "mfma", "mixtral_prefill_q8g128": "mfma"}
 CSRC = os.path.join(ROOT, "expert_ffn_layer_router_amd", "csrc")
 STREAM_MAX_TOKENS = 64   # the library's decode (weight-streaming) family runs up to this T
 
@@ -73,8 +75,11 @@ def algorithmic_work(shape, counts):
     k, E = shape.top_k + ns, shape.num_experts          # rows per token; routed experts
     R = T * k
     active = int(sum(1 for c in counts if c > 0))
-    gate_up_w = active * (d * f + 2 * 2 * 2 * f)       # gate+up codes (2 x d*f/2) + fp16 s,z of both
-    down_w = active * (d * f // 2 + 2 * 2 * d)          # down codes + fp16 s,z
+    bits, G = shape.bits, shape.group
+    gu_groups = d // G if G else 1                      # (s, z) per output row and group
+    dn_groups = f // G if G else 1
+    gate_up_w = active * (2 * f * d * bits // 8 + 2 * 2 * 2 * f * gu_groups)   # gate+up codes + fp16 s,z of both
+    down_w = active * (d * f * bits // 8 + 2 * 2 * d * dn_groups)              # down codes + fp16 s,z
     gate_up_bytes = gate_up_w + 2 * T * d + 2 * R * f   # + x rows read, h written (bf16)
     down_bytes = down_w + 2 * R * f + 2 * R * d         # + h read, y written (bf16-equivalent)
     layer_bytes = gate_up_w + down_w + 2 * T * d + 2 * T * d + 4 * E * d + 4 * E + 4 * (E + ns)
@@ -103,7 +108,7 @@ def cpu_baseline(case, budget_s=15.0):
     while True:
         t0 = time.perf_counter()
         oracle.forward(case.hidden, top_k=shape.top_k, precision="f32", tokens=tokens,
-                       num_shared=shape.num_shared, **kw)
+                       num_shared=shape.num_shared, bits=shape.bits, group=shape.group, **kw)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() > t_end or len(times) >= 5:
             break
@@ -309,7 +314,7 @@ def main(argv=None):
     rb = None if w.router_b is None else to_device(w.router_b)
     st = to_device(w.slot_table)
     probe = MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T,
-                     num_shared=shape.num_shared)
+                     num_shared=shape.num_shared, weight_bits=shape.bits, group_size=shape.group)
     ws = probe.new_workspace(T)
     out = torch.empty((T, shape.d_model), dtype=torch.bfloat16, device="cuda")
 
@@ -327,7 +332,8 @@ def main(argv=None):
         f"{rot} weight-pool copies of {pool_bytes / 1e6:.1f} MB")
 
     layers = [MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T,
-                       num_shared=shape.num_shared) for _ in range(rot)]
+                       num_shared=shape.num_shared, weight_bits=shape.bits, group_size=shape.group)
+              for _ in range(rot)]
     stream = torch.cuda.Stream()
     multi = None
     if args.mode == "graph":
@@ -427,7 +433,8 @@ def main(argv=None):
         "config": {"workload": args.config, "T": T, "d_model": shape.d_model, "d_ff": shape.d_ff,
                    "num_experts": shape.num_experts, "top_k": shape.top_k, "num_shared": shape.num_shared,
                    "num_slots": shape.num_slots,
-                   "weights": "int4 codes + fp16 scale/zero-point per output row",
+                   "weights": (f"{'int4' if shape.bits == 4 else '8-bit'} codes + fp16 scale/zero-point per "
+                               + ("output row" if not shape.group else f"output row and {shape.group}-input group")),
                    "mode": {"layers": f"HIP graph of {rot} consecutive layers (own weights each), replayed",
                             "graph": "one HIP graph per layer step", "eager": "eager launches"}[args.mode],
                    "weight_pool_copies": rot, "parallelism": "single GPU"},

@@ -24,7 +24,8 @@ STAGE_NAMES = ("router", "regroup", "gate_up", "down", "combine")
 class MoeConfig(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("num_slots", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("num_shared", ctypes.c_int32)]
+                ("flags", ctypes.c_uint32), ("num_shared", ctypes.c_int32), ("weight_bits", ctypes.c_int32),
+                ("group_size", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):

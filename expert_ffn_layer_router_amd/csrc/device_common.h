@@ -75,6 +75,56 @@ __device__ __forceinline__ u32x4 codes_to_bf16(uint32_t w) {
   return r;
 }
 
+// 8-bit codes on the load path: bytes k0..k3 in w0 and k4..k7 in w1 -> the
+// bf16 pairs (k0, k4), (k1, k5), (k2, k6), (k3, k7), the fragment k-order
+// above.  A code 0..255 has at most 8 significant bits, so it converts to
+// fp32 exactly (v_cvt_f32_ubyteN) and its bf16 pattern is the top half of the
+// fp32 one (one v_perm_b32 per pair); the MFMA accumulates sum_k a_k q_k and
+// the epilogue applies s * (acc - z * sum_k a_k).
+__device__ __forceinline__ float code_byte_f32(uint32_t w, int i) { return (float)((w >> (8 * i)) & 0xFFu); }
+__device__ __forceinline__ uint32_t pack_exact_bf16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+__device__ __forceinline__ u32x4 bytes_to_bf16(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  r.x = pack_exact_bf16(code_byte_f32(w0, 0), code_byte_f32(w1, 0));
+  r.y = pack_exact_bf16(code_byte_f32(w0, 1), code_byte_f32(w1, 1));
+  r.z = pack_exact_bf16(code_byte_f32(w0, 2), code_byte_f32(w1, 2));
+  r.w = pack_exact_bf16(code_byte_f32(w0, 3), code_byte_f32(w1, 3));
+  return r;
+}
+
+// Codes to bf16(q f + m), in the fragment order of codes_to_bf16 /
+// bytes_to_bf16 (the conversion rounds to nearest even).  With f = 1 and
+// m = -z (integer z) this is q - z, exact: |q - z| <= 255 has at most 8
+// significant bits; f = 0, m = 0 gives zeros.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+__device__ __forceinline__ u32x4 dequant_int4_bf16(uint32_t w, float s, float m) {
+  const uint32_t t0 = w & 0x0F0F0F0Fu, t1 = (w >> 4) & 0x0F0F0F0Fu;  // k0 k2 k4 k6 / k1 k3 k5 k7
+  u32x4 r;
+  r.x = pack_bf16_rne(fmaf(code_byte_f32(t0, 0), s, m), fmaf(code_byte_f32(t0, 2), s, m));  // (k0, k4)
+  r.y = pack_bf16_rne(fmaf(code_byte_f32(t1, 0), s, m), fmaf(code_byte_f32(t1, 2), s, m));  // (k1, k5)
+  r.z = pack_bf16_rne(fmaf(code_byte_f32(t0, 1), s, m), fmaf(code_byte_f32(t0, 3), s, m));  // (k2, k6)
+  r.w = pack_bf16_rne(fmaf(code_byte_f32(t1, 1), s, m), fmaf(code_byte_f32(t1, 3), s, m));  // (k3, k7)
+  return r;
+}
+__device__ __forceinline__ u32x4 dequant_int8_bf16(uint32_t w0, uint32_t w1, float s, float m) {
+  u32x4 r;
+  r.x = pack_bf16_rne(fmaf(code_byte_f32(w0, 0), s, m), fmaf(code_byte_f32(w1, 0), s, m));
+  r.y = pack_bf16_rne(fmaf(code_byte_f32(w0, 1), s, m), fmaf(code_byte_f32(w1, 1), s, m));
+  r.z = pack_bf16_rne(fmaf(code_byte_f32(w0, 2), s, m), fmaf(code_byte_f32(w1, 2), s, m));
+  r.w = pack_bf16_rne(fmaf(code_byte_f32(w0, 3), s, m), fmaf(code_byte_f32(w1, 3), s, m));
+  return r;
+}
+
+// Offset the widened codes carry: 128 for int4 (128 + q), none for 8-bit.
+template <int BITS>
+constexpr float code_bias() { return BITS == 4 ? kCodeBias : 0.0f; }
+
 // bf16 1.0 in every slot: a B operand whose product gives row sums of A.
 __device__ __forceinline__ u32x4 ones_bf16() {
   u32x4 r;

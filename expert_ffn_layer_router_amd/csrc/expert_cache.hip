@@ -140,18 +140,21 @@ MOE_EXPORT moe_status moe_expert_upload(moe_handle h, const moe_weights* pool, i
   if (!pool || !src) return moe::api_fail(MOE_ERR_INVALID_ARG, "null pointer argument");
   if (slot < 0 || slot >= cfg->num_slots)
     return moe::api_fail(MOE_ERR_INVALID_ARG, "slot %d outside [0, num_slots=%d)", slot, cfg->num_slots);
-  const size_t d = (size_t)cfg->d_model, f = (size_t)cfg->d_ff;
+  const size_t d = (size_t)cfg->d_model, f = (size_t)cfg->d_ff, bits = (size_t)cfg->weight_bits;
+  // (s, z) per output row, or per output row and group of group_size inputs
+  const size_t gu_groups = cfg->group_size ? d / cfg->group_size : 1;
+  const size_t dn_groups = cfg->group_size ? f / cfg->group_size : 1;
   struct Part {
     void* dst;
     const void* src;
     size_t bytes;
   };
   const Part parts[] = {
-      {(void*)pool->w_gate, src->w_gate, f * d / 2}, {(void*)pool->w_up, src->w_up, f * d / 2},
-      {(void*)pool->w_down, src->w_down, d * f / 2}, {(void*)pool->s_gate, src->s_gate, 2 * f},
-      {(void*)pool->z_gate, src->z_gate, 2 * f},     {(void*)pool->s_up, src->s_up, 2 * f},
-      {(void*)pool->z_up, src->z_up, 2 * f},         {(void*)pool->s_down, src->s_down, 2 * d},
-      {(void*)pool->z_down, src->z_down, 2 * d},
+      {(void*)pool->w_gate, src->w_gate, f * d * bits / 8},   {(void*)pool->w_up, src->w_up, f * d * bits / 8},
+      {(void*)pool->w_down, src->w_down, d * f * bits / 8},   {(void*)pool->s_gate, src->s_gate, 2 * f * gu_groups},
+      {(void*)pool->z_gate, src->z_gate, 2 * f * gu_groups},  {(void*)pool->s_up, src->s_up, 2 * f * gu_groups},
+      {(void*)pool->z_up, src->z_up, 2 * f * gu_groups},      {(void*)pool->s_down, src->s_down, 2 * d * dn_groups},
+      {(void*)pool->z_down, src->z_down, 2 * d * dn_groups},
   };
   for (const Part& p : parts)
     if (!p.dst || !p.src) return moe::api_fail(MOE_ERR_INVALID_ARG, "null weight pointer");

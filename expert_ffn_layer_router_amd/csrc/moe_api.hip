@@ -93,7 +93,7 @@ moe_status api_fail(moe_status st, const char* fmt, ...) {
 }
 bool api_check_handle(moe_handle h, const moe_config** cfg) {
   if (!h || h->magic != kMagic) return false;
-  *cfg = &h->cfg;
+  *cfg = &h->ecfg;  // the normalised shape (weight_bits 4 or 8)
   return true;
 }
 }  // namespace moe
@@ -277,12 +277,17 @@ MOE_EXPORT moe_status moe_create(const moe_config* cfg, moe_handle* out) {
   if (c.num_shared < 0 || c.top_k + c.num_shared > 8 || c.num_experts + c.num_shared > 256)
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "num_shared=%d: need >= 0, top_k + num_shared <= 8 and "
                 "num_experts + num_shared <= 256", c.num_shared);
+  if (c.weight_bits != 0 && c.weight_bits != 4 && c.weight_bits != 8)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "weight_bits=%d must be 0, 4 or 8", c.weight_bits);
+  if (c.group_size != 0 && c.group_size != 128)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "group_size=%d must be 0 or 128", c.group_size);
   moe_layer* h = new (std::nothrow) moe_layer;
   if (!h) return fail(MOE_ERR_INVALID_ARG, "out of host memory");
   h->cfg = c;
   h->ecfg = c;
   h->ecfg.num_experts = c.num_experts + c.num_shared;
   h->ecfg.top_k = c.top_k + c.num_shared;
+  if (h->ecfg.weight_bits == 0) h->ecfg.weight_bits = 4;
   *out = h;
   return MOE_OK;
 }

@@ -36,8 +36,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kBM = kPrefillTileRows;   // 128 rows per block
 constexpr int kBK = 64;                 // k per stage
 constexpr int kARow = kBK * 2;          // 128 bytes of an activation row per stage
-constexpr int kWRow = kBK / 2;          // 32 bytes of a weight row per stage
 constexpr int kABytes = kBM * kARow;    // 16 KB
+constexpr int kQGroup = 128;            // k per (s, z) group of the grouped formats
 #ifndef MOE_PF_GU_STAGES
 #define MOE_PF_GU_STAGES 2
 #endif
@@ -79,6 +79,10 @@ constexpr int kPrefillDownWaves = MOE_PF_DN_NW;
 __device__ __forceinline__ void load_lds16(const void* g, char* lds_base) {
   __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds_base, 16, 0, 0);
 }
+// 4 bytes: lane l of the wave writes lds_base + 4 l.
+__device__ __forceinline__ void load_lds4(const void* g, char* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds_base, 4, 0, 0);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
@@ -87,9 +91,13 @@ __device__ __forceinline__ void wait_vmem() {
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// swizzled chunk positions: activation rows hold 8 chunks of 16 B, weight rows 2
+// swizzled chunk positions: activation rows hold 8 chunks of 16 B, weight rows
+// 2 (int4) or 4 (8-bit)
 __device__ __forceinline__ int apos(int row, int c) { return c ^ ((row >> 1) & 7); }
-__device__ __forceinline__ int wpos(int row, int c) { return c ^ ((row >> 3) & 1); }
+template <int BITS>
+__device__ __forceinline__ int wpos(int row, int c) {
+  return BITS == 4 ? c ^ ((row >> 3) & 1) : c ^ ((row >> 1) & 3);
+}
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -123,14 +131,33 @@ struct PrefillArgs {
 // for the same columns), so every widened weight fragment feeds MI matrix-core
 // products and every staged activation byte feeds 64 NJ weight rows.  kNBuf
 // LDS stage buffers (kNBuf - 1 stages in flight); OCC blocks per compute unit.
-template <bool GATEUP, int NJ, int kNBuf, int OCC, int WN, int NW>
+//
+// BITS: int4 or 8-bit codes (a stage holds 32 or 64 bytes of every weight
+// row).  Per-row formats widen the codes exactly and apply (s, z) in the
+// epilogue.  GROUPED (one (s, z) per output row and 128-k group): every
+// stage also copies the (s, z) of its group for the block's weight rows into
+// LDS; the codes are widened to q - z (exact in bf16: at most 8 significant
+// bits), and each accumulator is kept in units of its column's current group
+// scale: at a group boundary it is multiplied by s_old / s_new (one fp32
+// rounding per group), and the epilogue multiplies by the last scale.  So
+// every weight enters the matrix cores exactly and no second set of
+// accumulators is needed.  A zero scale zeroes its group's codes and keeps
+// the previous scale.
+template <bool GATEUP, int NJ, int kNBuf, int OCC, int WN, int NW, int BITS, bool GROUPED>
 __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs a) {
+  static_assert(BITS == 4 || BITS == 8, "int4 or 8-bit codes");
   constexpr int kThreads = 64 * NW;
   constexpr int kWRows = 64 * NJ;             // weight rows per block
+  constexpr int kWRow = kBK * BITS / 8;       // bytes of a weight row per stage
+  constexpr int kCPR = kWRow / 16;            // 16-byte chunks per weight row
   constexpr int kWBytes = kWRows * kWRow;
-  constexpr int kStage = kABytes + kWBytes;
+  constexpr int kPBytes = GROUPED ? 256 * NW : 0;  // (s, z) of the stage's group: 256 bytes per wave
+  constexpr int kStage = kABytes + kWBytes + kPBytes;
   constexpr int kAI = (kABytes / 1024) / NW;  // activation-load instructions (1 KB) per wave per stage
   constexpr int kWI = (kWBytes / 1024) / NW;  // weight-load instructions per wave per stage
+  constexpr int kPI = GROUPED ? 1 : 0;        // (s, z) load instructions (256 B) per wave per stage
+  constexpr float kBias = code_bias<BITS>();
+  static_assert(!GROUPED || 2 * kWRows * 2 <= kPBytes, "the (s, z) of a stage fit");
   constexpr int WM = NW / WN;                 // waves along the rows
   constexpr int MI = (kBM / 32) / WM;         // row blocks of 32 per wave
   constexpr int NJW = (kWRows / 32) / WN;     // weight-row blocks of 32 per wave
@@ -163,7 +190,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
     }
     return;
   }
-  const size_t wrow_bytes = (size_t)K / 2;
+  const size_t wrow_bytes = (size_t)K * BITS / 8;
 
   // activation rows this lane copies: 16 instructions of 8 rows per stage, kAI per wave
   const uint8_t* asrc[kAI];
@@ -175,18 +202,31 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
                                   : a.act + (size_t)(pbase + rr) * a.dff;
     asrc[j] = reinterpret_cast<const uint8_t*>(rowp) + 16 * apos(r, lane % 8);
   }
-  // weight rows: 2 NJ instructions of 32 rows per stage, kWI per wave
+  // weight rows: instructions of 64 / kCPR rows per stage, kWI per wave
   const uint8_t* wsrc[kWI];
 #pragma unroll
   for (int j = 0; j < kWI; ++j) {
-    const int r = (wave * kWI + j) * 32 + lane / 2;
+    const int r = (wave * kWI + j) * (64 / kCPR) + lane / kCPR;
     const uint8_t* base = a.w0;
     int n = n0 + r;
     if (GATEUP) {
       base = r < kWRows / 2 ? a.w0 : a.w1;
       n = n0 + (r % (kWRows / 2));
     }
-    wsrc[j] = base + ((size_t)slot * ncols + n) * wrow_bytes + 16 * wpos(r, lane % 2);
+    wsrc[j] = base + ((size_t)slot * ncols + n) * wrow_bytes + 16 * wpos<BITS>(r, lane % kCPR);
+  }
+  // grouped: the (s, z) of the stage's group, entries e = 0 .. 2 kWRows - 1
+  // in LDS (e < kWRows: s of block weight row e, then z), 2 entries per lane;
+  // waves past the last entry copy duplicates into the spare end of the area
+  const int ngroups = K / kQGroup;
+  const uint8_t* psrc = nullptr;
+  if constexpr (GROUPED) {
+    const int e = (wave * 128 + 2 * lane) % (2 * kWRows);
+    const int r = e % kWRows;
+    const bool zp = e >= kWRows;
+    const uint16_t* arr = (!GATEUP || r < kWRows / 2) ? (zp ? a.z0 : a.s0) : (zp ? a.z1 : a.s1);
+    const int n = n0 + (GATEUP ? r % (kWRows / 2) : r);
+    psrc = reinterpret_cast<const uint8_t*>(arr + (size_t)slot * ngroups * ncols + n);
   }
   // row sums of A for the zero-point term
   if (tid < kBM) {
@@ -217,6 +257,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
     for (int j = 0; j < kWI; ++j)
       load_lds16(wsrc[j] + (size_t)st * kWRow, buf + kABytes + (wave * kWI + j) * 1024);
+    if constexpr (GROUPED)
+      load_lds4(psrc + (size_t)(st * kBK / kQGroup) * ncols * 2, buf + kABytes + kWBytes + wave * 256);
   };
 
   f32x16 acc[MI][NJW];
@@ -231,6 +273,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
   for (int j = 0; j < NJW; ++j)
     wr[j] = GATEUP ? (j < HJ ? 32 * HJ * wn + 32 * j : kWRows / 2 + 32 * HJ * wn + 32 * (j - HJ)) : 32 * NJW * wn + 32 * j;
+
+  // grouped formats: per weight-row block of this wave, the scale its sums
+  // are kept in, and the current group's code factor (1, or 0 for a zero
+  // scale) and offset (-z times it)
+  float cur_s[NJW], gf[NJW], gm[NJW];
+#pragma unroll
+  for (int j = 0; j < NJW; ++j) cur_s[j] = gf[j] = 1.0f, gm[j] = 0.0f;
 
   // row blocks of 32 of this wave that hold rows of the tile (the rest are
   // skipped: a tile's last rows may be missing)
@@ -250,20 +299,57 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
       // past stage st - 1, so its buffer can be refilled with stage st + kNBuf - 1
       const int later = min(kNBuf - 2, nst - 1 - st);
       if (kNBuf > 3 && later >= 2)
-        wait_vmem<(kNBuf > 3 ? 2 : 0) * (kAI + kWI)>();
+        wait_vmem<(kNBuf > 3 ? 2 : 0) * (kAI + kWI + kPI)>();
       else if (kNBuf > 2 && later >= 1)
-        wait_vmem<(kNBuf > 2 ? 1 : 0) * (kAI + kWI)>();
+        wait_vmem<(kNBuf > 2 ? 1 : 0) * (kAI + kWI + kPI)>();
       else
         wait_vmem<0>();
       lds_barrier();
       if (st + kNBuf - 1 < nst) issue(st + kNBuf - 1);
       const char* buf = smem + (st % kNBuf) * kStage;
-      u32x4 bq[NJW];
+      // this lane's codes of the stage: step s uses word s (int4) or words 2s, 2s + 1 (8-bit)
+      u32x4 bq[NJW][kCPR / 2];
 #pragma unroll
       for (int j = 0; j < NJW; ++j) {
         const int r = wr[j] + l32;
-        bq[j] = *reinterpret_cast<const u32x4*>(buf + kABytes + r * kWRow + 16 * wpos(r, hh));
+#pragma unroll
+        for (int c = 0; c < kCPR / 2; ++c)
+          bq[j][c] = *reinterpret_cast<const u32x4*>(buf + kABytes + r * kWRow +
+                                                     16 * wpos<BITS>(r, (kCPR / 2) * hh + c));
       }
+      if constexpr (GROUPED) {
+        if ((st * kBK) % kQGroup == 0) {  // first stage of a group: its (s, z), rescale the sums
+          const uint16_t* pz = reinterpret_cast<const uint16_t*>(buf + kABytes + kWBytes);
+#pragma unroll
+          for (int j = 0; j < NJW; ++j) {
+            const int r = wr[j] + l32;
+            const float sj = fp16_to_f32(pz[r]), zj = fp16_to_f32(pz[kWRows + r]);
+            const bool live = sj != 0.0f;
+            const float rho = live ? cur_s[j] / sj : 1.0f;
+            cur_s[j] = live ? sj : cur_s[j];
+            gf[j] = live ? 1.0f : 0.0f;
+            gm[j] = -zj * gf[j];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+              if (i < ML) acc[i][j] *= rho;
+          }
+        }
+      }
+      auto widen = [&](int j, int s) {
+        const uint32_t w0 = bq[j][(BITS / 4) * s / 4][((BITS / 4) * s) % 4];
+        if constexpr (BITS == 4) {
+          if constexpr (GROUPED)
+            return dequant_int4_bf16(w0, gf[j], gm[j]);  // q - z, or 0 for a zero scale
+          else
+            return codes_to_bf16(w0);
+        } else {
+          const uint32_t w1 = bq[j][(2 * s + 1) / 4][(2 * s + 1) % 4];
+          if constexpr (GROUPED)
+            return dequant_int8_bf16(w0, w1, gf[j], gm[j]);
+          else
+            return bytes_to_bf16(w0, w1);
+        }
+      };
       // A fragments (fragment order already) of step s; the next step's are read
       // before this step's products, so the LDS latency hides behind them
       auto read_a = [&](int s, u32x4(&av)[MI]) {
@@ -282,7 +368,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
         if (s + 1 < 4) read_a(s + 1, nxt);
 #pragma unroll
         for (int j = 0; j < NJW; ++j) {
-          const u32x4 b = codes_to_bf16(bq[j][s]);
+          const u32x4 b = widen(j, s);
 #pragma unroll
           for (int i = 0; i < MI; ++i)
             if (i < ML) acc[i][j] = mfma32(cur[i], b, acc[i][j]);
@@ -316,8 +402,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
     for (int jj = 0; jj < HJ; ++jj) {
       const int nl = 32 * HJ * wn + 32 * jj + l32;  // column inside the block (n0 is a multiple of 8)
       const size_t sidx = (size_t)slot * ncols + n0 + nl;
-      const float sg = fp16_to_f32(a.s0[sidx]), cg = kCodeBias + fp16_to_f32(a.z0[sidx]);
-      const float su = fp16_to_f32(a.s1[sidx]), cu = kCodeBias + fp16_to_f32(a.z1[sidx]);
+      // grouped formats: the weights were dequantised in full already
+      const float sg = GROUPED ? cur_s[jj] : fp16_to_f32(a.s0[sidx]);
+      const float cg = GROUPED ? 0.0f : kBias + fp16_to_f32(a.z0[sidx]);
+      const float su = GROUPED ? cur_s[jj + HJ] : fp16_to_f32(a.s1[sidx]);
+      const float cu = GROUPED ? 0.0f : kBias + fp16_to_f32(a.z1[sidx]);
       const int hcol = h_phys_col(nl);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
@@ -370,8 +459,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
     for (int j = 0; j < NJW; ++j) {
       const size_t sidx = (size_t)slot * ncols + n0 + 32 * NJW * wn + 32 * j + l32;
-      sd[j] = fp16_to_f32(a.s0[sidx]);
-      cd[j] = kCodeBias + fp16_to_f32(a.z0[sidx]);
+      sd[j] = GROUPED ? cur_s[j] : fp16_to_f32(a.s0[sidx]);
+      cd[j] = GROUPED ? 0.0f : kBias + fp16_to_f32(a.z0[sidx]);
     }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -406,7 +495,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
     for (int j = 0; j < NJW; ++j) {
       const int n = n0 + 32 * NJW * wn + 32 * j + l32;
       const size_t sidx = (size_t)slot * ncols + n;
-      const float sd = fp16_to_f32(a.s0[sidx]), cd = kCodeBias + fp16_to_f32(a.z0[sidx]);
+      const float sd = GROUPED ? cur_s[j] : fp16_to_f32(a.s0[sidx]);
+      const float cd = GROUPED ? 0.0f : kBias + fp16_to_f32(a.z0[sidx]);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -423,6 +513,18 @@ namespace {
 // gate/up blocks are 32 NJ output columns wide: the wide block when d_ff allows it
 bool gateup_wide(const moe_config& c) { return c.d_ff % (32 * kPrefillGateUpNJ) == 0; }
 int gateup_blocks(const moe_config& c) { return c.d_ff / (gateup_wide(c) ? 32 * kPrefillGateUpNJ : 128); }
+// Calls f(bits, grouped) with the weight format as compile-time constants.
+template <class F>
+void with_format(const moe_config& c, F&& f) {
+  using std::integral_constant;
+  if (c.weight_bits == 8) {
+    if (c.group_size) f(integral_constant<int, 8>{}, integral_constant<bool, true>{});
+    else f(integral_constant<int, 8>{}, integral_constant<bool, false>{});
+  } else {
+    if (c.group_size) f(integral_constant<int, 4>{}, integral_constant<bool, true>{});
+    else f(integral_constant<int, 4>{}, integral_constant<bool, false>{});
+  }
+}
 }  // namespace
 
 void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w,
@@ -449,11 +551,15 @@ void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* h
   a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
   a.hparts = gateup_blocks(c);
   dim3 grid(a.hparts, p.max_tiles);
-  if (gateup_wide(c))
-    prefill_gemm_kernel<true, kPrefillGateUpNJ, kPrefillGateUpStages, kPrefillGateUpBlocks, MOE_PF_GU_WN,
-                        kPrefillGateUpWaves><<<grid, 64 * kPrefillGateUpWaves, 0, s>>>(a);
-  else
-    prefill_gemm_kernel<true, 4, 2, 2, 4, 4><<<grid, 256, 0, s>>>(a);
+  with_format(c, [&](auto bits, auto grouped) {
+    constexpr int B = decltype(bits)::value;
+    constexpr bool G = decltype(grouped)::value;
+    if (gateup_wide(c))
+      prefill_gemm_kernel<true, kPrefillGateUpNJ, kPrefillGateUpStages, kPrefillGateUpBlocks, MOE_PF_GU_WN,
+                          kPrefillGateUpWaves, B, G><<<grid, 64 * kPrefillGateUpWaves, 0, s>>>(a);
+    else
+      prefill_gemm_kernel<true, 4, 2, 2, 4, 4, B, G><<<grid, 256, 0, s>>>(a);
+  });
 }
 
 void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& w, char* ws, hipStream_t s) {
@@ -472,12 +578,17 @@ void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& 
   a.z0 = w.z_down;
   a.y = reinterpret_cast<uint16_t*>(ws + p.y);
   a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
-  if (c.d_model % (64 * MOE_PF_DN_NJ) == 0) {
-    prefill_gemm_kernel<false, MOE_PF_DN_NJ, kPrefillDownStages, kPrefillDownBlocks, MOE_PF_DN_WN, kPrefillDownWaves>
-        <<<dim3(c.d_model / (64 * MOE_PF_DN_NJ), p.max_tiles), 64 * kPrefillDownWaves, 0, s>>>(a);
-  } else {
-    prefill_gemm_kernel<false, 2, 2, 2, 2, 4><<<dim3(c.d_model / 128, p.max_tiles), 256, 0, s>>>(a);
-  }
+  with_format(c, [&](auto bits, auto grouped) {
+    constexpr int B = decltype(bits)::value;
+    constexpr bool G = decltype(grouped)::value;
+    if (c.d_model % (64 * MOE_PF_DN_NJ) == 0) {
+      prefill_gemm_kernel<false, MOE_PF_DN_NJ, kPrefillDownStages, kPrefillDownBlocks, MOE_PF_DN_WN,
+                          kPrefillDownWaves, B, G>
+          <<<dim3(c.d_model / (64 * MOE_PF_DN_NJ), p.max_tiles), 64 * kPrefillDownWaves, 0, s>>>(a);
+    } else {
+      prefill_gemm_kernel<false, 2, 2, 2, 2, 4, B, G><<<dim3(c.d_model / 128, p.max_tiles), 256, 0, s>>>(a);
+    }
+  });
 }
 
 }  // namespace moe

@@ -44,9 +44,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kStageK = 256;                  // k per stage
-constexpr int kWRowBytes = kStageK / 2;       // int4 bytes of one weight row per stage
+constexpr int kWRowBytes = 128;              // bytes of one weight row per stage (256 int4 or 128 8-bit codes)
 constexpr int kRowsPerWInst = 1024 / kWRowBytes;  // weight rows per 1 KB load instruction (8)
+constexpr int kQGroup = 128;                 // k per (s, z) group of the grouped formats
+constexpr int kPBytes = 1024;                // grouped formats: (s, z) bytes staged per stage
 
 // 16 bytes from global memory to LDS: lane l of the wave writes lds_base + 16 l.
 // NT: with the non-temporal hint, for lines read once per launch: they are
@@ -55,6 +56,10 @@ constexpr int kRowsPerWInst = 1024 / kWRowBytes;  // weight rows per 1 KB load i
 template <bool NT>
 __device__ __forceinline__ void load_lds16(const void* g, char* lds_base) {
   __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds_base, 16, 0, NT ? 2 /* nt */ : 0);
+}
+// 4 bytes: lane l of the wave writes lds_base + 4 l.
+__device__ __forceinline__ void load_lds4(const void* g, char* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds_base, 4, 0, 0);
 }
 
 // Wait until at most `n` vector-memory operations of this wave are pending.
@@ -90,6 +95,12 @@ __device__ __forceinline__ u32x2 lds_read8(const char* p) {
   u32x2 v;
   const uint32_t addr = (uint32_t)(uintptr_t)(const lds_void*)p;
   asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+__device__ __forceinline__ uint32_t lds_read_u16(const char* p) {
+  uint32_t v;
+  const uint32_t addr = (uint32_t)(uintptr_t)(const lds_void*)p;
+  asm volatile("ds_read_u16 %0, %1" : "=v"(v) : "v"(addr));
   return v;
 }
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -164,23 +175,45 @@ __device__ void fused_combine_tail(const StreamArgs& a, int bx, int ntiles) {
 // RG row groups of 16 per tile (tiles of up to 16 RG rows of one expert): a
 // widened weight fragment then feeds RG matrix-core products, so an expert's
 // weights are streamed once for up to 16 RG of its rows.
-template <bool GATEUP, int NCW, int NBUF, int KW, bool NT, int RG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RG == 1 ? MOE_STREAM_WPE : 3)))
+//
+// BITS: int4 codes (two per byte, widened with codes_to_bf16) or 8-bit codes
+// (bytes_to_bf16); a stage is 128 bytes of every weight row either way (256
+// or 128 k).  GROUPED: one (s, z) per output row and group of 128 k, in
+// [K/128][N] arrays.  A wave's k part of a stage then lies in one group, so
+// the wave multiplies it into accumulators of its own, turns them into
+// s (acc - (bias + z) sum_k a) with that group's (s, z) and adds that to its
+// running sums; the (s, z) of a stage's groups are copied into LDS beside
+// its weights (one more 1 KB copy per stage).  Per-row formats apply (s, z)
+// once, in the epilogue.
+template <bool GATEUP, int NCW, int NBUF, int KW, bool NT, int RG, int BITS, bool GROUPED>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(GROUPED ? (RG == 1 ? 3 : 2) : (RG == 1 ? MOE_STREAM_WPE : 3))))
 void stream_gemm_kernel(StreamArgs a) {
   static_assert(NBUF == 2 || NBUF == 3, "stage ring of 2 or 3 buffers");
   static_assert(KW == 2 || KW == 4, "k split over 2 or 4 waves");
   static_assert(RG == 1 || RG == 2, "tiles of 16 or 32 rows");
+  static_assert(BITS == 4 || BITS == 8, "int4 or 8-bit codes");
+  static_assert(!GROUPED || NCW == 1, "grouped formats run 64-column blocks");
+  constexpr int SK = kWRowBytes * 8 / BITS;             // k per stage
   constexpr int COLS = 64 * NCW;                        // output columns per block
   constexpr int NWR = (GATEUP ? 2 : 1) * COLS;          // weight rows per stage
-  constexpr int WBYTES = NWR * kWRowBytes;              // one stage buffer
+  constexpr int WBYTES = NWR * kWRowBytes;              // weights of one stage
+  constexpr int PBYTES = GROUPED ? kPBytes : 0;         // (s, z) of one stage
+  constexpr int SBYTES = WBYTES + PBYTES;               // one stage buffer
   constexpr int WI = NWR / kRowsPerWInst / 4;           // weight-load instructions per wave per stage
   constexpr int CW = 4 / KW;                            // column parts
   constexpr int CT = COLS / 16 / CW;                    // 16-column tiles per wave and weight matrix
   constexpr int NB = (GATEUP ? 2 : 1) * CT;             // B fragments per wave per stage
-  constexpr int KR = kStageK / KW;                      // k per wave per stage
+  constexpr int KR = SK / KW;                           // k per wave per stage
   constexpr int KS = KR / 32;                           // MFMA k-steps per wave per stage (16 B of A each)
+  constexpr int WPS = BITS / 4;                         // 32-bit code words per lane and k-step
+  constexpr int LB = KS * WPS * 4;                      // code bytes per lane and weight row per stage
+  constexpr float kBias = code_bias<BITS>();
+  static_assert(KS >= 1 && (LB == 8 || LB == 16), "lane slices of 8 or 16 code bytes");
+  static_assert(!GROUPED || (kQGroup % KR == 0 && SK <= 2 * kQGroup), "a wave's k part lies in one group");
+  static_assert(!GROUPED || 4 * 2 * COLS * 2 == kPBytes, "4 arrays x 2 groups x 64 columns of fp16 per stage");
   static_assert(WI * kRowsPerWInst * 4 == NWR, "even split over waves");
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * WBYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * SBYTES];
 
   const int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;  // column slice, row tile, k-split
   const int ntiles = *a.num_tiles;
@@ -195,7 +228,7 @@ void stream_gemm_kernel(StreamArgs a) {
   const int ncols_total = GATEUP ? a.dff : a.d;
   const int K = GATEUP ? a.d : a.kchunk;
   const int kbeg = GATEUP ? 0 : bz * a.kchunk;
-  const size_t row_bytes = (size_t)(GATEUP ? a.d : a.dff) / 2;
+  const size_t row_bytes = (size_t)(GATEUP ? a.d : a.dff) * BITS / 8;
   const bool bad = slot < 0 || slot >= a.num_slots;
   float* yrow = GATEUP ? nullptr : a.ypart + ((size_t)bz * a.R + pbase) * a.d;
 
@@ -220,18 +253,31 @@ void stream_gemm_kernel(StreamArgs a) {
       const int r = (wave * WI + j) * kRowsPerWInst + lane / 8;  // block weight row
       const uint8_t* base = (!GATEUP || r < COLS) ? a.w0 : a.w1;
       const int n = n0 + (r % COLS);
-      wsrc[j] = base + ((size_t)slot * ncols_total + n) * row_bytes + kbeg / 2 + 16 * wchunk_pos(r, lane % 8);
+      wsrc[j] = base + ((size_t)slot * ncols_total + n) * row_bytes + (size_t)kbeg * BITS / 8 +
+                16 * wchunk_pos(r, lane % 8);
     }
-    const int nst = (K + kStageK - 1) / kStageK;
-    const bool half_last = (K % kStageK) != 0;  // the last stage has only its lower 128 k
-    const bool idle_half = KR * kp >= kStageK / 2;  // this wave has no k in a half stage
+    // grouped: wave w copies 256 bytes of every stage's (s, z) -- array w
+    // (gate/up: s_gate, z_gate, s_up, z_up; down: s, z, s, z), the block's 64
+    // columns of the stage's groups 0 and 1 (lane / 32), 2 columns per lane;
+    // in LDS: [array][group of the stage][column]
+    const int ngroups = (GATEUP ? a.d : a.dff) / kQGroup;
+    const uint8_t* psrc = nullptr;
+    if constexpr (GROUPED) {
+      const bool up = GATEUP && wave >= 2;
+      const uint16_t* arr = (wave & 1) ? (up ? a.z1 : a.z0) : (up ? a.s1 : a.s0);
+      psrc = reinterpret_cast<const uint8_t*>(arr + (size_t)slot * ngroups * ncols_total + n0 + 2 * (lane % 32));
+    }
+    const int nst = (K + SK - 1) / SK;
+    const bool half_last = (K % SK) != 0;  // the last stage has only its lower half of k
+    const bool idle_half = KR * kp >= SK / 2;  // this wave has no k in a half stage
     // The copies are issued without per-lane conditions, so that the
     // compiler's own wait for the activation registers is exact: a half
     // stage copies its upper 4 chunks from the lower ones (into LDS nobody
     // reads), and lanes of rows past the tile's end load row 0 (their
-    // registers only reach output rows that are never stored).
+    // registers only reach output rows that are never stored).  A stage's
+    // second group past the matrix's last re-reads the last (unused).
     auto issue_w = [&](int st) {
-      char* buf = smem + (st % NBUF) * WBYTES;
+      char* buf = smem + (st % NBUF) * SBYTES;
       const bool half = half_last && st == nst - 1;
 #pragma unroll
       for (int j = 0; j < WI; ++j) {
@@ -239,12 +285,16 @@ void stream_gemm_kernel(StreamArgs a) {
         const int back = (half && wchunk_pos(r, lane % 8) >= 4) ? 64 : 0;
         load_lds16<NT>(wsrc[j] + (size_t)st * kWRowBytes - back, buf + (wave * WI + j) * 1024);
       }
+      if constexpr (GROUPED) {
+        const int gi = min((kbeg + st * SK) / kQGroup + lane / 32, ngroups - 1);
+        load_lds4(psrc + (size_t)gi * ncols_total * 2, buf + WBYTES + wave * 256);
+      }
     };
     auto load_a = [&](int st, u32x4 (&av)[RG][KS]) {
       const int sa = (half_last && st == nst - 1 && idle_half) ? 0 : st;
 #pragma unroll
       for (int g = 0; g < RG; ++g) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(asrc[g] + (size_t)sa * kStageK);
+        const u32x4* src = reinterpret_cast<const u32x4*>(asrc[g] + (size_t)sa * SK);
 #pragma unroll
         for (int j = 0; j < KS; ++j) av[g][j] = src[j];
       }
@@ -258,17 +308,18 @@ void stream_gemm_kernel(StreamArgs a) {
       for (int t = 0; t < NB; ++t) acc[g][t] = f32x4{0, 0, 0, 0};
     }
     const u32x4 ones = ones_bf16();
-    // this lane's bytes of every weight row: (KR / 8) bytes at KR / 2 kp + (KR / 8) grp
-    const int boff = (KR / 2) * kp + (KR / 8) * grp;
+    // this lane's bytes of every weight row: LB bytes at (KR BITS / 8) kp + LB grp
+    const int boff = (KR * BITS / 8) * kp + LB * grp;
+    const int pgrp = GROUPED ? (KR * kp) / kQGroup : 0;  // group of this wave's k part inside a stage
     auto compute = [&](int st, const u32x4 (&acur)[RG][KS]) {
       if (half_last && st == nst - 1 && idle_half) return;
-      const char* buf = smem + (st % NBUF) * WBYTES;
-      uint32_t bw[NB][KS];
+      const char* buf = smem + (st % NBUF) * SBYTES;
+      uint32_t bw[NB][LB / 4];
 #pragma unroll
       for (int t = 0; t < NB; ++t) {
         const int r = (t >= CT ? COLS : 0) + 16 * (CT * cp + t % CT) + lr;
         const char* p = buf + r * kWRowBytes + 16 * wchunk_pos(r, boff / 16) + boff % 16;
-        if constexpr (KS == 4) {
+        if constexpr (LB == 16) {
           const u32x4 v = lds_read16(p);
           bw[t][0] = v.x; bw[t][1] = v.y; bw[t][2] = v.z; bw[t][3] = v.w;
         } else {
@@ -276,35 +327,89 @@ void stream_gemm_kernel(StreamArgs a) {
           bw[t][0] = v.x; bw[t][1] = v.y;
         }
       }
+      uint32_t ps[GROUPED ? NB : 1], pz[GROUPED ? NB : 1];
+      if constexpr (GROUPED) {
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const int q = (t >= CT ? 2 : 0);  // s of gate (or down) / up; z follows
+          const int nl = 16 * (CT * cp + t % CT) + lr;
+          ps[t] = lds_read_u16(buf + WBYTES + ((q * 2 + pgrp) * 64 + nl) * 2);
+          pz[t] = lds_read_u16(buf + WBYTES + (((q + 1) * 2 + pgrp) * 64 + nl) * 2);
+        }
+      }
       lds_wait();
 #pragma unroll
       for (int t = 0; t < NB; ++t)
 #pragma unroll
-        for (int j = 0; j < KS; ++j) lds_ready(bw[t][j]);
+        for (int j = 0; j < LB / 4; ++j) lds_ready(bw[t][j]);
+      if constexpr (GROUPED) {
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          lds_ready(ps[t]);
+          lds_ready(pz[t]);
+        }
+      }
       u32x4 x[RG][KS];
 #pragma unroll
       for (int g = 0; g < RG; ++g)
 #pragma unroll
-        for (int j = 0; j < KS; ++j) {
-          x[g][j] = GATEUP ? permute_a(acur[g][j]) : acur[g][j];  // h is stored in fragment order already
-          accs[g] = mfma16(x[g][j], ones, accs[g]);
+        for (int j = 0; j < KS; ++j) x[g][j] = GATEUP ? permute_a(acur[g][j]) : acur[g][j];  // h is in fragment order
+      auto widen = [&](int t, int j) {
+        if constexpr (BITS == 4)
+          return codes_to_bf16(bw[t][j]);
+        else
+          return bytes_to_bf16(bw[t][2 * j], bw[t][2 * j + 1]);
+      };
+      if constexpr (!GROUPED) {
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+          for (int j = 0; j < KS; ++j) accs[g] = mfma16(x[g][j], ones, accs[g]);
+#pragma unroll
+        for (int t = 0; t < NB; ++t)
+#pragma unroll
+          for (int j = 0; j < KS; ++j) {
+            const u32x4 b = widen(t, j);
+#pragma unroll
+            for (int g = 0; g < RG; ++g) acc[g][t] = mfma16(x[g][j], b, acc[g][t]);
+          }
+      } else {
+        // this stage's products and row sums, then s (acc - (bias + z) sum a)
+        f32x4 sacc[RG][NB], ssum[RG];
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+          ssum[g] = f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < KS; ++j) ssum[g] = mfma16(x[g][j], ones, ssum[g]);
+#pragma unroll
+          for (int t = 0; t < NB; ++t) sacc[g][t] = f32x4{0, 0, 0, 0};
         }
 #pragma unroll
-      for (int t = 0; t < NB; ++t)
+        for (int t = 0; t < NB; ++t)
 #pragma unroll
-        for (int j = 0; j < KS; ++j) {
-          const u32x4 b = codes_to_bf16(bw[t][j]);
+          for (int j = 0; j < KS; ++j) {
+            const u32x4 b = widen(t, j);
 #pragma unroll
-          for (int g = 0; g < RG; ++g) acc[g][t] = mfma16(x[g][j], b, acc[g][t]);
+            for (int g = 0; g < RG; ++g) sacc[g][t] = mfma16(x[g][j], b, sacc[g][t]);
+          }
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const float sg = fp16_to_f32((uint16_t)ps[t]), cg = kBias + fp16_to_f32((uint16_t)pz[t]);
+#pragma unroll
+          for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[g][t][i] += sg * (sacc[g][t][i] - cg * ssum[g][i]);
         }
+      }
     };
 
     // Issue order: A(0), W(0) .. W(NBUF - 2); then at stage s, A(s + 1) and
-    // W(s + NBUF - 1).  At stage s the copies younger than W(s) are at least
-    // A(s + 1) and W(s + 1) (NBUF = 2), or W(s + 1), A(s + 1) and W(s + 2)
-    // (NBUF = 3), so waiting until that many are pending completes W(s).
-    // The last NBUF - 1 stages issue no weight copies and wait for all.
-    constexpr int kPending = (NBUF - 1) * WI + RG * KS;
+    // W(s + NBUF - 1) (each W with its (s, z) copy for the grouped formats).
+    // At stage s the copies younger than W(s) are at least A(s + 1) and
+    // W(s + 1) (NBUF = 2), or W(s + 1), A(s + 1) and W(s + 2) (NBUF = 3), so
+    // waiting until that many are pending completes W(s).  The last NBUF - 1
+    // stages issue no weight copies and wait for all.
+    constexpr int kPending = (NBUF - 1) * (WI + (GROUPED ? 1 : 0)) + RG * KS;
     u32x4 anx[RG][KS], acur[RG][KS];
     load_a(0, anx);
     issue_w(0);
@@ -322,15 +427,16 @@ void stream_gemm_kernel(StreamArgs a) {
       compute(st, acur);
       lds_barrier();
     }
-    // scale and code offset (128 + z) of this wave's columns, loaded while the last stages land
+    // per-row formats: scale and code offset (bias + z) of this wave's
+    // columns, loaded while the last stages land (grouped: already applied)
     const size_t sbase = (size_t)slot * ncols_total + n0;
     float sc[NB], cc[NB];
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const int nl = 16 * (CT * cp + t % CT) + lr;  // column inside the block
       const bool up = GATEUP && t >= CT;
-      sc[t] = fp16_to_f32((up ? a.s1 : a.s0)[sbase + nl]);
-      cc[t] = kCodeBias + fp16_to_f32((up ? a.z1 : a.z0)[sbase + nl]);
+      sc[t] = GROUPED ? 1.0f : fp16_to_f32((up ? a.s1 : a.s0)[sbase + nl]);
+      cc[t] = GROUPED ? 0.0f : kBias + fp16_to_f32((up ? a.z1 : a.z0)[sbase + nl]);
     }
     for (int st = nmain; st < nst; ++st) {
 #pragma unroll
@@ -344,13 +450,13 @@ void stream_gemm_kernel(StreamArgs a) {
       lds_barrier();
     }
 
-    // Every wave turns its k part into s (acc - (128 + z) sum_k a) -- linear
+    // Every wave turns its k part into s (acc - (bias + z) sum_k a) -- linear
     // in the k parts -- and hands it over through LDS (the ring is free, one
     // row group at a time); the KW waves of a column part then add the k
     // parts in fixed order, each for the column tiles it owns (local tile tl
     // with tl % KW == kp).
     float* part = reinterpret_cast<float*>(smem);  // [wave][tile][4][64]
-    static_assert(4 * NB * 4 * 64 * 4 <= NBUF * WBYTES, "the k-part hand-over fits the stage ring");
+    static_assert(4 * NB * 4 * 64 * 4 <= NBUF * SBYTES, "the k-part hand-over fits the stage ring");
     uint16_t* hrow = GATEUP ? a.h + (size_t)pbase * a.dff + n0 : nullptr;
     float* ybase = GATEUP ? nullptr : yrow + n0;
 #pragma unroll
@@ -406,15 +512,36 @@ namespace {
 // and early eviction keeps the activations and the router's inputs (read
 // again by the next layer step) in the caches.  Measured to help every
 // decode shape, multi-tile experts included.
-template <bool GATEUP, int NCW>
+template <bool GATEUP, int NCW, int BITS, bool GROUPED>
 void launch_stream(const moe_config& c, const Plan& p, const StreamArgs& args, hipStream_t s) {
   const int ncols = GATEUP ? c.d_ff : c.d_model;
   dim3 grid(ncols / (64 * NCW), p.max_tiles, GATEUP ? 1 : p.down_split);
   constexpr int KW = GATEUP ? MOE_STREAM_KW_GU : MOE_STREAM_KW_DN;
   if (p.tile_rows == 2 * kStreamTileRows)
-    stream_gemm_kernel<GATEUP, NCW, MOE_STREAM_NBUF, KW, true, 2><<<grid, 256, 0, s>>>(args);
+    stream_gemm_kernel<GATEUP, NCW, MOE_STREAM_NBUF, KW, true, 2, BITS, GROUPED><<<grid, 256, 0, s>>>(args);
   else
-    stream_gemm_kernel<GATEUP, NCW, MOE_STREAM_NBUF, KW, true, 1><<<grid, 256, 0, s>>>(args);
+    stream_gemm_kernel<GATEUP, NCW, MOE_STREAM_NBUF, KW, true, 1, BITS, GROUPED><<<grid, 256, 0, s>>>(args);
+}
+
+// The weight format picks the kernel; the grouped formats run 64-column blocks.
+template <bool GATEUP>
+void launch_stream_format(const moe_config& c, const Plan& p, const StreamArgs& a, int ncw, hipStream_t s) {
+  const bool grouped = c.group_size != 0;
+  if (c.weight_bits == 8) {
+    if (grouped)
+      launch_stream<GATEUP, 1, 8, true>(c, p, a, s);
+    else if (ncw == 2)
+      launch_stream<GATEUP, 2, 8, false>(c, p, a, s);
+    else
+      launch_stream<GATEUP, 1, 8, false>(c, p, a, s);
+  } else {
+    if (grouped)
+      launch_stream<GATEUP, 1, 4, true>(c, p, a, s);
+    else if (ncw == 2)
+      launch_stream<GATEUP, 2, 4, false>(c, p, a, s);
+    else
+      launch_stream<GATEUP, 1, 4, false>(c, p, a, s);
+  }
 }
 }  // namespace
 
@@ -438,10 +565,7 @@ void launch_gateup_stream(const moe_config& c, const Plan& p, const uint16_t* hi
   a.z1 = w.z_up;
   a.h = reinterpret_cast<uint16_t*>(ws + p.h);
   a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
-  if (p.gateup_ncw == 2)
-    launch_stream<true, 2>(c, p, a, s);
-  else
-    launch_stream<true, 1>(c, p, a, s);
+  launch_stream_format<true>(c, p, a, p.gateup_ncw, s);
 }
 
 void launch_down_stream(const moe_config& c, const Plan& p, const moe_weights& w, uint16_t* out, char* ws,
@@ -469,10 +593,7 @@ void launch_down_stream(const moe_config& c, const Plan& p, const moe_weights& w
     a.fc.T = p.T;
     a.fc.k = c.top_k;
   }
-  if (p.down_ncw == 2)
-    launch_stream<false, 2>(c, p, a, s);
-  else
-    launch_stream<false, 1>(c, p, a, s);
+  launch_stream_format<false>(c, p, a, p.down_ncw, s);
 }
 
 }  // namespace moe

@@ -34,7 +34,8 @@ def to_device(arr: np.ndarray, device="cuda"):
 
 @dataclasses.dataclass
 class DeviceWeights:
-    """The slot-indexed int4 weight pool on the device (keeps the tensors alive)."""
+    """The slot-indexed weight pool (codes, scales, zero-points) on the device
+    (keeps the tensors alive)."""
     tensors: dict
 
     @classmethod
@@ -51,9 +52,10 @@ class MoeLayer:
     moe_graph_capture / moe_graph_launch / moe_device_flags."""
 
     def __init__(self, d_model: int, d_ff: int, num_experts: int, top_k: int, num_slots: int,
-                 max_tokens: int, num_shared: int = 0):
+                 max_tokens: int, num_shared: int = 0, weight_bits: int = 4, group_size: int = 0):
         self.lib = _lib.load()
-        self.cfg = _lib.MoeConfig(d_model, d_ff, num_experts, top_k, num_slots, max_tokens, 0, num_shared)
+        self.cfg = _lib.MoeConfig(d_model, d_ff, num_experts, top_k, num_slots, max_tokens, 0, num_shared,
+                                  weight_bits, group_size)
         h = ctypes.c_void_p()
         _lib.check(self.lib.moe_create(ctypes.byref(self.cfg), ctypes.byref(h)))
         self.handle = h

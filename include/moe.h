@@ -4,8 +4,10 @@
  * One call evaluates, for T tokens,
  *     out[t] = sum over token t's k chosen experts e of w[t,e] * FFN_e(x[t]),
  *     FFN_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x)),
- * with the expert weights stored as per-row int4 codes plus an fp16 scale and
- * zero-point (W = (q - z) * s) and read through an expert-to-slot table.
+ * with the expert weights stored as integer codes plus fp16 scales and
+ * zero-points (W = (q - z) * s) and read through an expert-to-slot table.
+ * Weight formats: int4 or 8-bit codes, with one (s, z) per output row or per
+ * output row and group of 128 inputs.
  * Optional shared experts are added for every token with weight 1:
  *     out[t] += sum over s < num_shared of FFN_{E+s}(x[t]).
  *
@@ -17,6 +19,8 @@
  *   regrouping    Strata page, section 4.2 (tokens reordered by expert id)
  *   int4 experts  Strata page, section 3.1 (per-expert scale and zero-point,
  *                 dequantised on the load path, not in a kernel of its own)
+ *   8-bit, groups Co-inference page, section 5.1 (8-bit expert weights, the
+ *                 router in full precision, grouped quantisation)
  *   group GEMM    Strata page, section 3.2 (one batched product over the
  *                 experts' contiguous token groups)
  *   slots         Co-inference page, section 2.2 (experts held in GPU cache
@@ -77,19 +81,25 @@ typedef struct moe_config {
                            expert s has id E + s and the shape of a routed expert; every
                            token takes it with weight exactly 1, after its k routed ones.
                            Its weights are in pool slot slot_table[E + s]. */
+  int32_t weight_bits;  /* code width: 4 (int4; 0 also means 4) or 8 */
+  int32_t group_size;   /* 0: one (s, z) per output row; 128: one per output row and group of
+                           128 consecutive inputs (k) */
 } moe_config;
 
 /* Per-slot weight pool (device pointers, caller-owned).  Slot s of a matrix
- * with N output rows and K inputs occupies N*K/2 bytes: row n holds K codes
- * in 0..15, two per byte, the even k in the low nibble.  Scales and
- * zero-points are fp16, one per output row, indexed by slot. */
+ * with N output rows and K inputs occupies N*K*B/8 bytes (B = weight_bits):
+ * row n holds K codes in 0..2^B-1, int4 two per byte with the even k in the
+ * low nibble, 8-bit one per byte.  Scales and zero-points are fp16 (the
+ * zero-points integers), indexed by slot: [N] per slot with group_size 0,
+ * [K/128][N] per slot (group-major) with group_size 128.  Below, P(N, K)
+ * stands for that per-slot shape. */
 typedef struct moe_weights {
-  const uint8_t *w_gate;   /* [num_slots][d_ff][d_model/2] */
-  const uint8_t *w_up;     /* [num_slots][d_ff][d_model/2] */
-  const uint8_t *w_down;   /* [num_slots][d_model][d_ff/2] */
-  const uint16_t *s_gate, *z_gate;  /* [num_slots][d_ff] */
-  const uint16_t *s_up, *z_up;      /* [num_slots][d_ff] */
-  const uint16_t *s_down, *z_down;  /* [num_slots][d_model] */
+  const uint8_t *w_gate;   /* [num_slots][d_ff][d_model*B/8] */
+  const uint8_t *w_up;     /* [num_slots][d_ff][d_model*B/8] */
+  const uint8_t *w_down;   /* [num_slots][d_model][d_ff*B/8] */
+  const uint16_t *s_gate, *z_gate;  /* [num_slots] P(d_ff, d_model) */
+  const uint16_t *s_up, *z_up;      /* [num_slots] P(d_ff, d_model) */
+  const uint16_t *s_down, *z_down;  /* [num_slots] P(d_model, d_ff) */
 } moe_weights;
 
 /* Device pointers into a workspace after a forward with T tokens.  With S
@@ -112,7 +122,8 @@ typedef void *moe_stream; /* a hipStream_t */
  * allocation.  Returns MOE_ERR_UNSUPPORTED_SHAPE for shapes outside:
  * d_model % 128 == 0, d_ff % 128 == 0, 1 <= E <= 256, 1 <= k <= min(E, 8),
  * num_slots >= 1, 1 <= max_tokens <= 65536, flags == 0, num_shared >= 0,
- * k + num_shared <= 8, E + num_shared <= 256. */
+ * k + num_shared <= 8, E + num_shared <= 256, weight_bits in {0, 4, 8},
+ * group_size in {0, 128}. */
 moe_status moe_create(const moe_config *cfg, moe_handle *out);
 
 /* Frees the handle and any captured graph.  NULL is ignored. */

@@ -35,7 +35,8 @@ class GpuLayer:
         self.shape = shape
         self.weights = weights
         self.layer = MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots,
-                              max_tokens or max(shape.T, 1), num_shared=shape.num_shared)
+                              max_tokens or max(shape.T, 1), num_shared=shape.num_shared,
+                              weight_bits=shape.bits, group_size=shape.group)
         self.dw = DeviceWeights.upload(weights)
         self.router_w = to_device(weights.router_w)
         self.router_b = None if weights.router_b is None else to_device(weights.router_b)

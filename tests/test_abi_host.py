@@ -48,7 +48,8 @@ def test_status_strings(lib):
                                 dict(top_k=9, num_experts=9), dict(top_k=3, num_experts=2),
                                 dict(num_slots=0), dict(max_tokens=0), dict(max_tokens=65537), dict(flags=1),
                                 dict(num_shared=-1), dict(top_k=2, num_shared=7),
-                                dict(num_experts=256, top_k=1, num_shared=1)])
+                                dict(num_experts=256, top_k=1, num_shared=1), dict(weight_bits=2),
+                                dict(weight_bits=16), dict(group_size=64), dict(group_size=-1)])
 def test_create_rejects_unsupported_shapes(lib, kw):
     st, h = _create(lib, **kw)
     assert st == _lib.MOE_ERR_UNSUPPORTED_SHAPE, _lib.last_error()
@@ -57,7 +58,8 @@ def test_create_rejects_unsupported_shapes(lib, kw):
 
 
 @pytest.mark.parametrize("kw", [dict(top_k=2, num_shared=6), dict(num_experts=255, top_k=1, num_shared=1),
-                                dict(num_experts=1, top_k=1, num_shared=7)])
+                                dict(num_experts=1, top_k=1, num_shared=7), dict(weight_bits=8),
+                                dict(weight_bits=4, group_size=128), dict(weight_bits=8, group_size=128)])
 def test_create_accepts_shared_expert_limits(lib, kw):
     st, h = _create(lib, **kw)
     assert st == 0, _lib.last_error()

@@ -18,17 +18,19 @@ from test_gpu_parity import check_routing
 pytestmark = pytest.mark.gpu
 
 
-def test_refill_from_host_on_a_copy_stream_matches_the_oracle():
+@pytest.mark.parametrize("bits,group", [(4, 0), (8, 128)])
+def test_refill_from_host_on_a_copy_stream_matches_the_oracle(bits, group):
     torch = require_gpu()
     from expert_ffn_layer_router_amd import (DeviceWeights, ExpertCache, HostExpert, MOE_FLAG_BAD_SLOT, MoeLayer,
                                              to_device)
     L, T = 3, 2
-    shape = synth.LayerShape(T, 128, 256, 8, 2, 8, "identity", 0.0)
+    shape = synth.LayerShape(T, 128, 256, 8, 2, 8, "identity", 0.0, 0, bits, group)
     layers = [synth.make_weights(shape, seed=10 + i) for i in range(L)]
     host = [[HostExpert.from_pool(w, e) for e in range(shape.num_experts)] for w in layers]
     pool = DeviceWeights.upload(layers[0])          # 8 slots; their first contents are never used
     cache = ExpertCache(num_sets=2, ways=4, num_experts=shape.num_experts)   # layers 0 and 2 share set 0
-    g = MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T)
+    g = MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T,
+                 weight_bits=bits, group_size=group)
     ws = g.new_workspace(T)
     out = torch.empty((T, shape.d_model), dtype=torch.bfloat16, device="cuda")
     compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
@@ -57,7 +59,8 @@ def test_refill_from_host_on_a_copy_stream_matches_the_oracle():
                 assert g.device_flags(ws, T, stream=compute) == 0
                 reruns += 1
             res = {k: v.cpu().numpy() for k, v in g.routing(ws, T).items()}
-            ref = oracle.forward(x_bits, top_k=shape.top_k, precision="f64", **weights_kwargs(layers[i]))
+            ref = oracle.forward(x_bits, top_k=shape.top_k, precision="f64", bits=bits, group=group,
+                                 **weights_kwargs(layers[i]))
             check_routing(res, ref)
             assert_out_close(bf16_bits_to_f64(out), ref["out"])
     hits, misses = cache.stats()

@@ -42,12 +42,14 @@ def _oracle(case, hidden=None, **over):
     kw.update(over)
     prec = "f64" if case.shape.d_model * case.shape.d_ff <= 128 * 256 else "f32"
     return oracle.forward(case.hidden if hidden is None else hidden, top_k=case.shape.top_k, precision=prec,
-                          num_shared=case.shape.num_shared, **kw)
+                          num_shared=case.shape.num_shared, bits=case.shape.bits, group=case.shape.group, **kw)
 
 
 @pytest.mark.parametrize("name", ["tiny", "fine_tiny", "mixtral_decode", "phi35_skew", "fine_decode",
                                   "mixtral_prefill", "fine_prefill", "shared_tiny", "fine_shared_tiny",
-                                  "shared_decode", "shared_prefill"])
+                                  "shared_decode", "shared_prefill", "tiny_q4g128", "tiny_q8", "tiny_q8g128",
+                                  "mixtral_decode_q4g128", "mixtral_decode_q8g128", "phi35_skew_q8",
+                                  "mixtral_prefill_q4g128", "mixtral_prefill_q8g128"])
 def test_layer_parity(name):
     require_gpu()
     say(f"{name}: generating layer")
@@ -66,7 +68,9 @@ def test_layer_parity(name):
 @pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 3), ("tiny", 37), ("fine_tiny", 100),
                                     ("fine_tiny", 257), ("tiny", 1000), ("shared_tiny", 1),
                                     ("shared_tiny", 33), ("shared_tiny", 300), ("fine_shared_tiny", 64),
-                                    ("fine_shared_tiny", 65)])
+                                    ("fine_shared_tiny", 65), ("tiny_q4g128", 1), ("tiny_q4g128", 33),
+                                    ("tiny_q4g128", 65), ("tiny_q4g128", 300), ("tiny_q8", 40), ("tiny_q8", 200),
+                                    ("tiny_q8g128", 17), ("tiny_q8g128", 129)])
 def test_ragged_token_counts(name, T):
     require_gpu()
     case = synth.make_case(name, T=T)
@@ -240,3 +244,26 @@ def test_one_workspace_across_token_counts_keeps_control_words_zero():
         assert_out_close(bf16_bits_to_f64(out), ref["out"])
         idx = g.layer.routing(ws, T)["topk_idx"].cpu().numpy()
         np.testing.assert_array_equal(idx, ref["topk_idx"])
+
+
+@pytest.mark.parametrize("name,T", [("tiny_q4g128", 16), ("tiny_q4g128", 300), ("tiny_q8g128", 16),
+                                    ("tiny_q8g128", 300)])
+def test_zero_group_scales(name, T):
+    """Groups whose scale is 0 contribute nothing (the codes may be anything);
+    the prefill kernels keep their running sums in the previous group's scale."""
+    require_gpu()
+    case = synth.make_case(name, T=T)
+    w = case.weights
+    arrays = {f: getattr(w, f).copy() for f in ("s_gate", "s_up", "s_down")}
+    for e in range(case.shape.num_experts):
+        sl = int(w.slot_table[e])
+        arrays["s_gate"][sl, 0, ::3] = 0          # first group of every third gate row
+        arrays["s_up"][sl, 1, :] = 0              # the whole second group of up
+        arrays["s_down"][sl, 1:, 5] = 0           # all but the first group of down row 5
+    w2 = dataclasses.replace(w, **arrays)
+    case2 = synth.Case(name, case.shape, case.seed, case.hidden, w2)
+    say(f"{name}: zero group scales, T={T}")
+    res = GpuLayer(case.shape, w2, max_tokens=T).run(case.hidden)
+    ref = _oracle(case2)
+    check_routing(res, ref)
+    assert_out_close(res["out"], ref["out"])
