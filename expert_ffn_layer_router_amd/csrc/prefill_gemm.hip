@@ -151,11 +151,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
   constexpr int kWRow = kBK * BITS / 8;       // bytes of a weight row per stage
   constexpr int kCPR = kWRow / 16;            // 16-byte chunks per weight row
   constexpr int kWBytes = kWRows * kWRow;
-  constexpr int kPBytes = GROUPED ? 256 * NW : 0;  // (s, z) of the stage's group: 256 bytes per wave
+  // grouped: (s, z) of the stage's group, 2 kWRows fp16 entries, in 256-byte
+  // copies (4 bytes per lane), kPI per wave
+  constexpr int kPI = GROUPED ? (4 * kWRows + 256 * NW - 1) / (256 * NW) : 0;
+  constexpr int kPBytes = kPI * 256 * NW;
   constexpr int kStage = kABytes + kWBytes + kPBytes;
   constexpr int kAI = (kABytes / 1024) / NW;  // activation-load instructions (1 KB) per wave per stage
   constexpr int kWI = (kWBytes / 1024) / NW;  // weight-load instructions per wave per stage
-  constexpr int kPI = GROUPED ? 1 : 0;        // (s, z) load instructions (256 B) per wave per stage
   constexpr float kBias = code_bias<BITS>();
   static_assert(!GROUPED || 2 * kWRows * 2 <= kPBytes, "the (s, z) of a stage fit");
   constexpr int WM = NW / WN;                 // waves along the rows
@@ -217,16 +219,19 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
   }
   // grouped: the (s, z) of the stage's group, entries e = 0 .. 2 kWRows - 1
   // in LDS (e < kWRows: s of block weight row e, then z), 2 entries per lane;
-  // waves past the last entry copy duplicates into the spare end of the area
+  // copies past the last entry load duplicates into the spare end of the area
   const int ngroups = K / kQGroup;
-  const uint8_t* psrc = nullptr;
+  const uint8_t* psrc[kPI > 0 ? kPI : 1] = {};
   if constexpr (GROUPED) {
-    const int e = (wave * 128 + 2 * lane) % (2 * kWRows);
-    const int r = e % kWRows;
-    const bool zp = e >= kWRows;
-    const uint16_t* arr = (!GATEUP || r < kWRows / 2) ? (zp ? a.z0 : a.s0) : (zp ? a.z1 : a.s1);
-    const int n = n0 + (GATEUP ? r % (kWRows / 2) : r);
-    psrc = reinterpret_cast<const uint8_t*>(arr + (size_t)slot * ngroups * ncols + n);
+#pragma unroll
+    for (int q = 0; q < kPI; ++q) {
+      const int e = ((q * NW + wave) * 128 + 2 * lane) % (2 * kWRows);
+      const int r = e % kWRows;
+      const bool zp = e >= kWRows;
+      const uint16_t* arr = (!GATEUP || r < kWRows / 2) ? (zp ? a.z0 : a.s0) : (zp ? a.z1 : a.s1);
+      const int n = n0 + (GATEUP ? r % (kWRows / 2) : r);
+      psrc[q] = reinterpret_cast<const uint8_t*>(arr + (size_t)slot * ngroups * ncols + n);
+    }
   }
   // row sums of A for the zero-point term
   if (tid < kBM) {
@@ -257,8 +262,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
     for (int j = 0; j < kWI; ++j)
       load_lds16(wsrc[j] + (size_t)st * kWRow, buf + kABytes + (wave * kWI + j) * 1024);
-    if constexpr (GROUPED)
-      load_lds4(psrc + (size_t)(st * kBK / kQGroup) * ncols * 2, buf + kABytes + kWBytes + wave * 256);
+    if constexpr (GROUPED) {
+#pragma unroll
+      for (int q = 0; q < kPI; ++q)
+        load_lds4(psrc[q] + (size_t)(st * kBK / kQGroup) * ncols * 2, buf + kABytes + kWBytes + (q * NW + wave) * 256);
+    }
   };
 
   f32x16 acc[MI][NJW];
