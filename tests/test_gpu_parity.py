@@ -267,3 +267,18 @@ def test_zero_group_scales(name, T):
     ref = _oracle(case2)
     check_routing(res, ref)
     assert_out_close(res["out"], ref["out"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "fine_tiny", "tiny_q8g128"])
+def test_maximum_token_count(name):
+    """T = 65536, the largest max_tokens the library accepts (fine_tiny: 393216
+    routed rows through the multi-block regroup)."""
+    require_gpu()
+    T = 65536
+    case = synth.make_case(name, T=T)
+    say(f"{name}: T={T}")
+    res = GpuLayer(case.shape, case.weights, max_tokens=T).run(case.hidden)
+    ref = _oracle(case)
+    check_routing(res, ref)
+    assert res["flags"] == 0
+    assert_out_close(res["out"], ref["out"])
