@@ -113,6 +113,16 @@ def cpu_baseline(case, budget_s=15.0):
         if time.perf_counter() > t_end or len(times) >= 5:
             break
     med = statistics.median(times)
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.forward(case.hidden, top_k=shape.top_k, precision="f32", tokens=tokens,
+                           num_shared=shape.num_shared, bits=shape.bits, group=shape.group, **kw)
+            single = time.perf_counter() - t0
+    except Exception:  # pragma: no cover
+        single = None
     cpu = ""
     try:
         with open("/proc/cpuinfo") as fh:
@@ -121,8 +131,11 @@ def cpu_baseline(case, budget_s=15.0):
         pass
     sample = (f"{n_tok} of {shape.T} tokens of the same workload, full forward incl. dequant of the "
               f"experts they use, median of {len(times)} runs; host CPU: {cpu}")
-    return {"value": n_tok / med, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample,
-            "seconds_per_run": med}
+    res = {"value": n_tok / med, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample,
+           "seconds_per_run": med}
+    if single is not None:
+        res["single_thread"] = {"value": n_tok / single, "unit": "tokens/s", "seconds_per_run": single}
+    return res
 
 
 # --------------------------------------------------------------------------- PMC summaries
@@ -196,6 +209,54 @@ def copy_calibration(gib=1.0, reps=5):
 
 
 # --------------------------------------------------------------------------- main bench
+def achievable_peaks(shape, torch, reps=10):
+    """What plain library code reaches on this GPU, as a second yardstick next
+    to the vendor peaks: a 2 GiB device copy (read + write bytes / time, torch's
+    copy kernel) and a dense bf16 GEMM shaped like the gate/up product of the
+    workload's rows (hipBLASLt through torch.matmul)."""
+    n = 1 << 31
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst
+    M = max(256, -(-shape.T * (shape.top_k + shape.num_shared) // 256) * 256)
+    N, K = 2 * shape.d_ff, shape.d_model
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(K, N, device="cuda", dtype=torch.bfloat16)
+    c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    ev1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * M * N * K * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
+    return {"hbm_copy_gbs": copy_gbs, "bf16_gemm_tflops": gemm_tflops,
+            "bf16_gemm_shape": [M, N, K],
+            "how": "2 GiB torch device copy (read+write bytes); torch.matmul bf16 (hipBLASLt) of the gate/up shape"}
+
+
+def step_percentiles(step, stream, torch, n=60):
+    """p10 / p50 / p90 of single steps, each between its own pair of events."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for i, (e0, e1) in enumerate(evs):
+            e0.record(stream)
+            step(i)
+            e1.record(stream)
+    stream.synchronize()
+    ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    return {"p10": ts[n // 10], "p50": ts[n // 2], "p90": ts[(9 * n) // 10], "n": n}
+
+
 def run_refill(args, shape, w, pools, layer, step, stream, torch):
     """Slot-pool refill: one expert's weights copied from page-locked host
     memory into a pool slot on a copy stream (moe_expert_upload), timed alone,
@@ -267,6 +328,7 @@ def main(argv=None):
                          "graph); graph: one graph per layer step; eager: plain launches")
     ap.add_argument("--rotations", type=int, default=0, help="weight-pool copies (0: enough to defeat the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the copy / library-GEMM yardsticks")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--refill", action="store_true",
@@ -425,6 +487,19 @@ def main(argv=None):
     roof["algorithmic_flops"] = work[dom]["flops"]
     roof["traffic"] = load_traffic(args.config, kernel_of_stage(dom, T))
 
+    # single-step latency spread, and the yardsticks plain library code reaches
+    if args.mode == "layers":
+        per = step_percentiles(lambda i: step(i * rot), stream, torch)
+        per = {key: (v / rot if key != "n" else v) for key, v in per.items()}
+    else:
+        per = step_percentiles(step, stream, torch)
+    peaks = None
+    if not args.no_peaks:
+        peaks = achievable_peaks(shape, torch)
+        ref = peaks["hbm_copy_gbs"] if roof["bound"] == "hbm" else peaks["bf16_gemm_tflops"]
+        roof["frac_of_achievable"] = roof["achieved"] / ref
+        log(f"achievable: copy {peaks['hbm_copy_gbs']:.0f} GB/s, bf16 GEMM {peaks['bf16_gemm_tflops']:.0f} TFLOP/s")
+
     layer_s = ms_per_step * 1e-3
     result = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -444,6 +519,8 @@ def main(argv=None):
                   "mfma_frac": work["layer"]["flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS,
                   "active_experts": work["active"], "stage_us": stage_us,
                   "event_us_per_step": 1e3 * ev_ms / args.steps},
+        "step_us": per,
+        "achievable": peaks,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
