@@ -282,3 +282,36 @@ def test_maximum_token_count(name):
     check_routing(res, ref)
     assert res["flags"] == 0
     assert_out_close(res["out"], ref["out"])
+
+
+@pytest.mark.parametrize("bits,group,T", [(4, 128, 16), (4, 128, 300), (8, 128, 300), (8, 0, 300)])
+def test_narrow_layer_formats(bits, group, T):
+    """d = 128: one k-group for the gate/up inputs and the narrow (128-column)
+    prefill down kernel, for every weight format."""
+    require_gpu()
+    shape = synth.LayerShape(T, 128, 256, 8, 2, 8, "identity", 0.0, 0, bits, group)
+    w = synth.make_weights(shape, seed=5)
+    x = synth.make_hidden(T, 128, seed=5)
+    case = synth.Case("narrow", shape, 5, x, w)
+    say(f"narrow d=128: bits={bits} group={group} T={T}")
+    res = GpuLayer(shape, w, max_tokens=T).run(x)
+    ref = _oracle(case)
+    check_routing(res, ref)
+    assert_out_close(res["out"], ref["out"])
+
+
+@pytest.mark.parametrize("T", [64, 4096])
+def test_one_hot_expert_takes_every_token(T):
+    """A router bias that sends every token's first choice to expert 5: one
+    group of T rows (32 row tiles at T = 4096), the others share the second
+    choices."""
+    require_gpu()
+    case = synth.make_case("fine_tiny", T=T)
+    b = np.zeros(case.shape.num_experts, np.float32)
+    b[5] = 50.0
+    say(f"fine_tiny: one hot expert, T={T}")
+    res = gpu_layer(case).run(case.hidden, router_b=b)
+    ref = _oracle(case, router_b=b)
+    assert np.all(ref["topk_idx"][:, 0] == 5) and ref["counts"][5] == T
+    check_routing(res, ref)
+    assert_out_close(res["out"], ref["out"])
