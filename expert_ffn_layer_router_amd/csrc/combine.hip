@@ -21,16 +21,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   if (idx >= (size_t)T * per_row) return;
   const int t = (int)(idx / per_row);
   const int c = (int)(idx % per_row) * 8;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int p = inv[(size_t)t * k + j];
-    const float w = topk_w[(size_t)t * k + j];
-    const u32x4 v = *reinterpret_cast<const u32x4*>(y + (size_t)p * d + c);
-    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+  // all k row indices and weights first, then all k row loads in flight at
+  // once, then the sums in order j = 0..k-1 (k <= 8 is uniform: no divergence)
+  int pos[8];
+  float wt[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(w, __uint_as_float(vw[i] << 16), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(w, __uint_as_float(vw[i] & 0xFFFF0000u), acc[2 * i + 1]);
+  for (int j = 0; j < 8; ++j) {
+    if (j < k) {
+      pos[j] = inv[(size_t)t * k + j];
+      wt[j] = topk_w[(size_t)t * k + j];
+    }
+  }
+  u32x4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < k) v[j] = *reinterpret_cast<const u32x4*>(y + (size_t)pos[j] * d + c);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < k) {
+      const uint32_t vw[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(wt[j], __uint_as_float(vw[i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wt[j], __uint_as_float(vw[i] & 0xFFFF0000u), acc[2 * i + 1]);
+      }
     }
   }
   u32x4 o;
