@@ -122,10 +122,12 @@ void make_plan(const moe_config& c, int T, Plan* p) {
     // one 512-k pass per wave: k-split in multiples of 128, up to kRouterSmallMaxSplit
     p->small_split = largest_divisor_at_most(c.d_model / 128, std::max(1, std::min(kRouterSmallMaxSplit, c.d_model / 2048)));
   } else {
-    // 64-token x router_tile_experts(E) tiles; split k (in multiples of 32) until about 512 blocks
+    // 64-token x router_tile_experts(E) tiles; split k (in multiples of 32) until about
+    // MOE_ROUTER_BLOCKS blocks
     const int tiles = ((T + kRouterMfmaTokens - 1) / kRouterMfmaTokens) *
                       ((Er + router_tile_experts(Er) - 1) / router_tile_experts(Er));
-    p->router_split = largest_divisor_at_most(c.d_model / kRouterMfmaK, std::max(1, (512 + tiles - 1) / tiles));
+    p->router_split = largest_divisor_at_most(c.d_model / kRouterMfmaK,
+                                              std::max(1, (MOE_ROUTER_BLOCKS + tiles - 1) / tiles));
   }
   // GEMM row tiles: sum_e ceil(c_e / rows) <= ceil(R / rows) + (non-empty experts)
   p->max_tiles = (p->R + p->tile_rows - 1) / p->tile_rows + std::min(E, p->R);

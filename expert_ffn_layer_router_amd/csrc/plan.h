@@ -15,6 +15,9 @@ constexpr int kRouterTokTile = 16;     // tokens per router wave
 constexpr int kRouterSmallMaxSplit = 4;  // few-token router: at most this many k-splits
 constexpr int kRouterMfmaTokens = 64;  // many-token router: tokens per block tile (16 per wave)
 constexpr int kRouterMfmaK = 32;       // many-token router: k per LDS chunk
+#ifndef MOE_ROUTER_BLOCKS
+#define MOE_ROUTER_BLOCKS 512          // many-token router: k-split until about this many blocks
+#endif
 // many-token router: experts per block tile (a multiple of 16, the MFMA width)
 inline int router_tile_experts(int E) { return E > 32 ? 64 : (E > 16 ? 32 : 16); }
 constexpr int kPrefillTileRows = 128;  // prefill family: rows of an expert group per GEMM tile
