@@ -77,6 +77,9 @@ def load():
         "moe_cache_request": (c_int, [vp, i32, vp, i32, vp, vp, vp, ctypes.POINTER(i32), vp]),
         "moe_cache_stats": (c_int, [vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
         "moe_expert_upload": (c_int, [vp, ctypes.POINTER(MoeWeights), i32, ctypes.POINTER(MoeWeights), vp]),
+        "moe_cache_geometry": (c_int, [ctypes.c_uint64, ctypes.c_uint64, i32, ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.POINTER(ctypes.c_int32)]),
+        "moe_expert_bytes": (c_int, [vp, ctypes.POINTER(ctypes.c_uint64)]),
         "moe_forward": (c_int, [vp, i32, vp, vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp, sz, vp]),
         "moe_routing_view": (c_int, [vp, vp, i32, ctypes.POINTER(MoeRouting)]),
         "moe_graph_capture": (c_int, [vp, i32, vp, vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp, sz, vp]),

@@ -133,6 +133,31 @@ MOE_EXPORT moe_status moe_cache_stats(moe_cache_handle c, int64_t* hits, int64_t
   return MOE_OK;
 }
 
+MOE_EXPORT moe_status moe_cache_geometry(uint64_t free_bytes, uint64_t expert_bytes, int32_t ways, int32_t* num_slots,
+                                         int32_t* num_sets) {
+  if (!num_slots || !num_sets) return moe::api_fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  if (expert_bytes == 0 || ways < 1)
+    return moe::api_fail(MOE_ERR_INVALID_ARG, "expert_bytes=%llu, ways=%d: need positive values",
+                         (unsigned long long)expert_bytes, ways);
+  const uint64_t slots = free_bytes / expert_bytes;
+  if (slots > (1u << 24)) return moe::api_fail(MOE_ERR_INVALID_ARG, "more than 2^24 slots");
+  *num_slots = (int32_t)slots;
+  *num_sets = (int32_t)(slots / (uint64_t)ways);
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_expert_bytes(moe_handle h, uint64_t* bytes) {
+  const moe_config* cfg = nullptr;
+  if (!moe::api_check_handle(h, &cfg)) return moe::api_fail(MOE_ERR_INVALID_ARG, "invalid handle");
+  if (!bytes) return moe::api_fail(MOE_ERR_INVALID_ARG, "null pointer argument");
+  const uint64_t d = (uint64_t)cfg->d_model, f = (uint64_t)cfg->d_ff, bits = (uint64_t)cfg->weight_bits;
+  const uint64_t gu_groups = cfg->group_size ? d / cfg->group_size : 1;
+  const uint64_t dn_groups = cfg->group_size ? f / cfg->group_size : 1;
+  // codes of gate, up and down, then fp16 scale and zero-point of each
+  *bytes = 3 * d * f * bits / 8 + 2 * 2 * (2 * f * gu_groups + d * dn_groups);
+  return MOE_OK;
+}
+
 MOE_EXPORT moe_status moe_expert_upload(moe_handle h, const moe_weights* pool, int32_t slot, const moe_weights* src,
                                         moe_stream stream) {
   const moe_config* cfg = nullptr;

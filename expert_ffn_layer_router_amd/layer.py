@@ -155,6 +155,12 @@ class MoeLayer:
         _lib.check(self.lib.moe_stage_times(self.handle, ms, _lib.MOE_NUM_STAGES, ctypes.byref(n)))
         return dict(zip(_lib.STAGE_NAMES, [float(v) for v in ms])), int(n.value)
 
+    def expert_bytes(self) -> int:
+        """Bytes of one expert's weights (one pool slot) in this layer's format."""
+        n = ctypes.c_uint64()
+        _lib.check(self.lib.moe_expert_bytes(self.handle, ctypes.byref(n)))
+        return n.value
+
     def upload_expert(self, pool: DeviceWeights, slot: int, src: "HostExpert", stream=None) -> None:
         """Enqueues the copies of one expert (host buffers) into pool slot `slot`."""
         _lib.check(self.lib.moe_expert_upload(self.handle, ctypes.byref(pool.struct()), int(slot),
@@ -193,6 +199,15 @@ class HostExpert:
 
 class ExpertCache:
     """The library's set-associative LRU cache of (layer, expert) over pool slots."""
+
+    @staticmethod
+    def geometry(free_bytes: int, expert_bytes: int, ways: int):
+        """(slots, sets) that fit `free_bytes` for experts of `expert_bytes`."""
+        lib = _lib.load()
+        s, n = ctypes.c_int32(), ctypes.c_int32()
+        _lib.check(lib.moe_cache_geometry(int(free_bytes), int(expert_bytes), int(ways), ctypes.byref(s),
+                                          ctypes.byref(n)))
+        return s.value, n.value
 
     def __init__(self, num_sets: int, ways: int, num_experts: int):
         self.lib = _lib.load()

@@ -236,6 +236,18 @@ moe_status moe_cache_request(moe_cache_handle c, int32_t layer, const int32_t *e
 /* Hits and misses over all requests so far. */
 moe_status moe_cache_stats(moe_cache_handle c, int64_t *hits, int64_t *misses);
 
+/* Pool geometry, Co-inference page, section 2.2: num_slots = floor(free_bytes
+ * / expert_bytes) slots in num_sets = floor(num_slots / ways) sets of `ways`
+ * (the remaining slots are left out of the cache).  Host arithmetic only.
+ * MOE_ERR_INVALID_ARG for a zero expert size, ways < 1 or more than 2^24
+ * slots. */
+moe_status moe_cache_geometry(uint64_t free_bytes, uint64_t expert_bytes, int32_t ways, int32_t *num_slots,
+                              int32_t *num_sets);
+
+/* Bytes of one expert's weights in the handle's format: the codes of gate, up
+ * and down plus their fp16 scales and zero-points (one pool slot). */
+moe_status moe_expert_bytes(moe_handle h, uint64_t *bytes);
+
 /* Enqueues on `stream` the copies of one expert's weights into pool slot
  * `slot` (0 <= slot < num_slots): `src` holds that expert alone, in the
  * moe_weights layout with a single slot, in host memory (page-locked, for the

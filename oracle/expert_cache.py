@@ -16,6 +16,8 @@ the experts a layer will need are copied host -> device on a second stream
 while the GPU computes, so the cache is asked for a layer's experts before
 that layer runs.
 
+cache_geometry gives (S, N) for a memory budget, an expert size and M.
+
 Readings where the page is silent (each is listed in the design notes):
   * the set of an expert of layer L is L mod N (the page's N indices cover
     the layers; with more layers than sets, layers share sets);
@@ -29,6 +31,16 @@ Readings where the page is silent (each is listed in the design notes):
     granularity;
   * a request needing more distinct experts than M at once is an error.
 """
+
+
+def cache_geometry(free_bytes: int, expert_bytes: int, ways: int):
+    """Co-inference page, section 2.2: S = floor(free memory / size of one
+    expert) slots, grouped into N = floor(S / M) sets of M ways.  Returns
+    (S, N); the slots past N * M stay unused."""
+    if free_bytes < 0 or expert_bytes <= 0 or ways <= 0:
+        raise ValueError("need free_bytes >= 0, expert_bytes > 0, ways > 0")
+    slots = free_bytes // expert_bytes
+    return slots, slots // ways
 
 
 class ExpertCacheModel:

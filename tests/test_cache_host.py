@@ -54,3 +54,31 @@ def test_create_rejects_bad_shapes():
     for args in ((0, 4, 8), (2, 0, 8), (2, 4, 0), (1 << 13, 1 << 12, 8)):
         assert lib.moe_cache_create(*args, ctypes.byref(h)) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_cache_create(2, 4, 8, None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_library_geometry_matches_the_model():
+    from oracle.expert_cache import cache_geometry
+    rng = random.Random(9)
+    for _ in range(200):
+        free = rng.randrange(0, 1 << 40)
+        expert = rng.randrange(1 << 20, 1 << 32)
+        ways = rng.randint(1, 16)
+        assert ExpertCache.geometry(free, expert, ways) == cache_geometry(free, expert, ways)
+    assert ExpertCache.geometry(19 << 30, 340 << 20, 4) == (57, 14)
+    with pytest.raises(_lib.MoeError):
+        ExpertCache.geometry(1 << 30, 0, 4)
+    with pytest.raises(_lib.MoeError):
+        ExpertCache.geometry(1 << 30, 1 << 20, 0)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 0), (4, 128), (8, 0), (8, 128)])
+def test_expert_bytes_is_the_size_of_one_pool_slot(bits, group):
+    """moe_expert_bytes == the bytes of one slot of the synthetic pool arrays."""
+    import synth
+    from expert_ffn_layer_router_amd import MoeLayer
+    shape = synth.LayerShape(4, 256, 384, 4, 2, 4, "identity", 0.0, 0, bits, group)
+    w = synth.make_weights(shape, seed=1)
+    layer = MoeLayer(256, 384, 4, 2, 4, 4, weight_bits=bits, group_size=group)
+    per_slot = sum(getattr(w, f)[0].nbytes for f in ("w_gate", "w_up", "w_down", "s_gate", "z_gate", "s_up",
+                                                     "z_up", "s_down", "z_down"))
+    assert layer.expert_bytes() == per_slot

@@ -96,3 +96,40 @@ def test_model_matches_history_brute_force(seed):
     c = ExpertCacheModel(num_sets, ways, E)
     got = [c.request(layer, ex) for layer, ex in seq]
     assert got == _history_lru(num_sets, ways, seq)
+
+
+def _golden(name):
+    import os
+    vals = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = (x.strip() for x in line.split("=", 1))
+                vals[k] = v
+    return vals
+
+
+def test_cache_geometry_reproduces_the_pages_worked_example():
+    """19 GB free, 340 MB experts: about 56 slots, and the (N, M) pairs (14, 4),
+    (11, 5), (7, 8) of the page's configuration table (binary units)."""
+    from oracle.expert_cache import cache_geometry
+    g = _golden("coinference_cache_sizing.txt")
+    free, expert = int(g["free_gb"]) << 30, int(g["expert_mb_mixtral"]) << 20
+    pairs = [tuple(int(x) for x in p.split("x")) for p in g["sets_ways"].split()]
+    for n, m in pairs:
+        slots, sets = cache_geometry(free, expert, m)
+        assert sets == n
+        assert abs(slots - int(g["slots_approx"])) <= 1
+        assert sets * m <= slots
+
+
+def test_page_expert_sizes_match_the_synthetic_shapes():
+    """One fp16 expert (gate, up, down) of the Mixtral-8x7B- and Phi-3.5-MoE-shaped
+    layers against the sizes the page prints (within its rounding, binary MB)."""
+    import synth
+    g = _golden("coinference_cache_sizing.txt")
+    for case, key in (("mixtral_decode", "expert_mb_mixtral"), ("phi35_skew", "expert_mb_phi35")):
+        shp = synth.case_shape(case)
+        fp16_bytes = 3 * shp.d_model * shp.d_ff * 2
+        assert abs(fp16_bytes / (1 << 20) / int(g[key]) - 1) < 0.02, (case, fp16_bytes)
