@@ -145,11 +145,12 @@ def test_out_of_range_shared_slot_sets_flag_and_contributes_zero(T):
     np.testing.assert_allclose(ref["out"], routed_only, rtol=0, atol=0)
 
 
-def test_deterministic_and_slot_permutation_invariant():
+@pytest.mark.parametrize("name,T", [("fine_tiny", 16), ("fine_tiny", 300), ("tiny_q8g128", 300)])
+def test_deterministic_and_slot_permutation_invariant(name, T):
     require_gpu()
-    case = synth.make_case("fine_tiny")
+    case = synth.make_case(name, T=T)
     g = gpu_layer(case)
-    say("fine_tiny: determinism")
+    say(f"{name}: determinism, T={T}")
     a = g.run(case.hidden)
     b = g.run(case.hidden)
     np.testing.assert_array_equal(a["out_bits"], b["out_bits"])
@@ -163,14 +164,25 @@ def test_deterministic_and_slot_permutation_invariant():
         arr[pi] = getattr(w, f)
         moved[f] = arr
     w2 = dataclasses.replace(w, slot_table=pi[w.slot_table].astype(np.int32), **moved)
-    say("fine_tiny: permuted pool")
+    say(f"{name}: permuted pool")
     c = GpuLayer(case.shape, w2, max_tokens=4096).run(case.hidden)
     np.testing.assert_array_equal(a["out_bits"], c["out_bits"])
 
 
-def test_graph_replay_matches_eager_and_reads_inputs_at_replay():
+_GRAPH_CASES = {
+    "fine_tiny": synth.case_shape("fine_tiny"),
+    # pools with room for a second copy of every expert (shared one included)
+    "q8g128_shared": synth.LayerShape(16, 256, 384, 8, 1, 24, "sparse", 1.0, 1, 8, 128),
+    "q4g128_prefill": synth.LayerShape(200, 256, 384, 8, 2, 16, "sparse", 1.0, 0, 4, 128),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_GRAPH_CASES))
+def test_graph_replay_matches_eager_and_reads_inputs_at_replay(name):
     torch = require_gpu()
-    case = synth.make_case("fine_tiny")
+    shape = _GRAPH_CASES[name]
+    T = shape.T
+    case = synth.Case(name, shape, 0, synth.make_hidden(T, shape.d_model, 0), synth.make_weights(shape, 0))
     g = gpu_layer(case)
     T, d = case.shape.T, case.shape.d_model
     x1 = case.hidden
@@ -194,7 +206,7 @@ def test_graph_replay_matches_eager_and_reads_inputs_at_replay():
     table = gl.to_device(w.slot_table)
     out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
     ws = gl.layer.new_workspace(T)
-    say("fine_tiny: capture")
+    say(f"{name}: capture, T={T}")
     with torch.cuda.stream(stream):
         gl.layer.capture(xb, gl.router_w, gl.router_b, table, gl.dw, out, ws, stream)
     for rep in range(3):
