@@ -8,9 +8,11 @@ JSON line on stdout; progress goes to stderr.
     python bench.py [--steps K] [--warmup W] [--config mixtral_decode] [--mode graph|eager]
 
 Inputs are seeded synthetic layers (synth package) resident in HBM before
-timing starts.  Several copies of the weight pool are used in rotation so
-that a step never finds the previous step's weights in the 256 MB MALL (a
-model's successive layers have different weights).
+timing starts.  By default one HIP graph replays 32 layers back to back, as
+a Mixtral-8x7B decode step would, each layer with its own copy of the weight
+pool, so that a step never finds the previous step's weights in the 256 MB
+MALL (a model's successive layers have different weights); the graph's own
+launch is then paid once per 32 layer steps.
 
 Extra modes for counter runs:
     --copy-calibration   time a plain 1 GiB device copy (scale for FETCH/WRITE_SIZE)
@@ -326,7 +328,11 @@ def main(argv=None):
     ap.add_argument("--mode", choices=["layers", "graph", "eager"], default="layers",
                     help="layers: one HIP graph replays the rotated layers back to back (a model's decode-step "
                          "graph); graph: one graph per layer step; eager: plain launches")
-    ap.add_argument("--rotations", type=int, default=0, help="weight-pool copies (0: enough to defeat the MALL)")
+    ap.add_argument("--rotations", type=int, default=0,
+                    help="weight-pool copies = layers in the layers-mode graph (0: --model-layers, and at least "
+                         "enough to defeat the MALL)")
+    ap.add_argument("--model-layers", type=int, default=32,
+                    help="MoE layers of the model's decode-step graph (Mixtral-8x7B: 32), each with its own weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the copy / library-GEMM yardsticks")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
@@ -386,7 +392,7 @@ def main(argv=None):
     counts = probe.routing(ws, T)["counts"].cpu().numpy()
     work = algorithmic_work(shape, counts)
     active_bytes = work["layer"]["bytes"]
-    rot = args.rotations or max(2, -(-int(1.5 * MALL_BYTES) // max(1, active_bytes)) + 1)
+    rot = args.rotations or max(2, args.model_layers, -(-int(1.5 * MALL_BYTES) // max(1, active_bytes)) + 1)
     rot = min(rot, max(1, int(60e9 // max(1, pool_bytes))))
     for _ in range(rot - 1):
         pools.append(DeviceWeights.upload(w))

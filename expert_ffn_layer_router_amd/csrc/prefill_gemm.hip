@@ -34,15 +34,16 @@ typedef __attribute__((address_space(1))) void glb_void;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = kPrefillTileRows;   // 128 rows per block
-constexpr int kBK = 64;                 // k per stage
-constexpr int kARow = kBK * 2;          // 128 bytes of an activation row per stage
-constexpr int kABytes = kBM * kARow;    // 16 KB
 constexpr int kQGroup = 128;            // k per (s, z) group of the grouped formats
 #ifndef MOE_PF_GU_STAGES
 #define MOE_PF_GU_STAGES 2
 #endif
 #ifndef MOE_PF_GU_BLOCKS
 #define MOE_PF_GU_BLOCKS 1
+#endif
+// k per stage of the int4 gate/up blocks (8-bit: 64, so that two stages fit the LDS)
+#ifndef MOE_PF_GU_BK4
+#define MOE_PF_GU_BK4 128
 #endif
 #ifndef MOE_PF_DN_STAGES
 #define MOE_PF_DN_STAGES 2
@@ -91,12 +92,16 @@ __device__ __forceinline__ void wait_vmem() {
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// swizzled chunk positions: activation rows hold 8 chunks of 16 B, weight rows
-// 2 (int4) or 4 (8-bit)
-__device__ __forceinline__ int apos(int row, int c) { return c ^ ((row >> 1) & 7); }
-template <int BITS>
-__device__ __forceinline__ int wpos(int row, int c) {
-  return BITS == 4 ? c ^ ((row >> 3) & 1) : c ^ ((row >> 1) & 3);
+// Swizzled position of 16-byte chunk c of a row of NC chunks in a stage
+// buffer (activation rows: 8 or 16 chunks; weight rows: 2, 4 or 8).  Eight
+// consecutive rows -- the lanes of one LDS cycle of a fragment read -- then
+// hit 8 different 16-byte bank groups.
+template <int NC>
+__device__ __forceinline__ int spos(int row, int c) {
+  if constexpr (NC == 2) return c ^ ((row >> 3) & 1);
+  else if constexpr (NC == 4) return c ^ ((row >> 1) & 3);
+  else if constexpr (NC == 8) return c ^ ((row >> 1) & 7);
+  else return c ^ (row & 7);
 }
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -143,10 +148,15 @@ struct PrefillArgs {
 // every weight enters the matrix cores exactly and no second set of
 // accumulators is needed.  A zero scale zeroes its group's codes and keeps
 // the previous scale.
-template <bool GATEUP, int NJ, int kNBuf, int OCC, int WN, int NW, int BITS, bool GROUPED>
+template <bool GATEUP, int NJ, int kNBuf, int OCC, int WN, int NW, int BITS, bool GROUPED, int kBK>
 __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs a) {
   static_assert(BITS == 4 || BITS == 8, "int4 or 8-bit codes");
+  static_assert(kBK == 64 || kBK == 128, "stages of 64 or 128 k");
   constexpr int kThreads = 64 * NW;
+  constexpr int kARow = kBK * 2;              // bytes of an activation row per stage
+  constexpr int kACh = kARow / 16;            // its 16-byte chunks
+  constexpr int kABytes = kBM * kARow;
+  constexpr int kNS = kBK / 16;               // matrix-core k-steps per stage
   constexpr int kWRows = 64 * NJ;             // weight rows per block
   constexpr int kWRow = kBK * BITS / 8;       // bytes of a weight row per stage
   constexpr int kCPR = kWRow / 16;            // 16-byte chunks per weight row
@@ -194,15 +204,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
   }
   const size_t wrow_bytes = (size_t)K * BITS / 8;
 
-  // activation rows this lane copies: 16 instructions of 8 rows per stage, kAI per wave
+  // activation rows this lane copies: instructions of 1024 / kARow rows per stage, kAI per wave
   const uint8_t* asrc[kAI];
 #pragma unroll
   for (int j = 0; j < kAI; ++j) {
-    const int r = (wave * kAI + j) * 8 + lane / 8;
+    const int r = (wave * kAI + j) * (64 / kACh) + lane / kACh;
     const int rr = r < rows ? r : 0;
     const uint16_t* rowp = GATEUP ? a.act + (size_t)(a.perm[pbase + rr] / a.topk) * a.d
                                   : a.act + (size_t)(pbase + rr) * a.dff;
-    asrc[j] = reinterpret_cast<const uint8_t*>(rowp) + 16 * apos(r, lane % 8);
+    asrc[j] = reinterpret_cast<const uint8_t*>(rowp) + 16 * spos<kACh>(r, lane % kACh);
   }
   // weight rows: instructions of 64 / kCPR rows per stage, kWI per wave
   const uint8_t* wsrc[kWI];
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
       base = r < kWRows / 2 ? a.w0 : a.w1;
       n = n0 + (r % (kWRows / 2));
     }
-    wsrc[j] = base + ((size_t)slot * ncols + n) * wrow_bytes + 16 * wpos<BITS>(r, lane % kCPR);
+    wsrc[j] = base + ((size_t)slot * ncols + n) * wrow_bytes + 16 * spos<kCPR>(r, lane % kCPR);
   }
   // grouped: the (s, z) of the stage's group, entries e = 0 .. 2 kWRows - 1
   // in LDS (e < kWRows: s of block weight row e, then z), 2 entries per lane;
@@ -315,7 +325,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
       lds_barrier();
       if (st + kNBuf - 1 < nst) issue(st + kNBuf - 1);
       const char* buf = smem + (st % kNBuf) * kStage;
-      // this lane's codes of the stage: step s uses word s (int4) or words 2s, 2s + 1 (8-bit)
+      // this lane's codes of the stage (k from kBK / 2 hh on): step s uses word s
+      // (int4) or words 2s, 2s + 1 (8-bit); its A chunk is kNS hh + s
       u32x4 bq[NJW][kCPR / 2];
 #pragma unroll
       for (int j = 0; j < NJW; ++j) {
@@ -323,7 +334,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
         for (int c = 0; c < kCPR / 2; ++c)
           bq[j][c] = *reinterpret_cast<const u32x4*>(buf + kABytes + r * kWRow +
-                                                     16 * wpos<BITS>(r, (kCPR / 2) * hh + c));
+                                                     16 * spos<kCPR>(r, (kCPR / 2) * hh + c));
       }
       if constexpr (GROUPED) {
         if ((st * kBK) % kQGroup == 0) {  // first stage of a group: its (s, z), rescale the sums
@@ -364,16 +375,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           const int r = 32 * MI * wm + 32 * i + l32;
-          if (i < ML) av[i] = *reinterpret_cast<const u32x4*>(buf + r * kARow + 16 * apos(r, 4 * hh + s));
+          if (i < ML) av[i] = *reinterpret_cast<const u32x4*>(buf + r * kARow + 16 * spos<kACh>(r, kNS * hh + s));
         }
       };
       u32x4 av0[MI], av1[MI];
       read_a(0, av0);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < kNS; ++s) {
         u32x4(&cur)[MI] = (s & 1) ? av1 : av0;
         u32x4(&nxt)[MI] = (s & 1) ? av0 : av1;
-        if (s + 1 < 4) read_a(s + 1, nxt);
+        if (s + 1 < kNS) read_a(s + 1, nxt);
 #pragma unroll
         for (int j = 0; j < NJW; ++j) {
           const u32x4 b = widen(j, s);
@@ -564,9 +575,10 @@ void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* h
     constexpr bool G = decltype(grouped)::value;
     if (gateup_wide(c))
       prefill_gemm_kernel<true, kPrefillGateUpNJ, kPrefillGateUpStages, kPrefillGateUpBlocks, MOE_PF_GU_WN,
-                          kPrefillGateUpWaves, B, G><<<grid, 64 * kPrefillGateUpWaves, 0, s>>>(a);
+                          kPrefillGateUpWaves, B, G, B == 4 ? MOE_PF_GU_BK4 : 64>
+          <<<grid, 64 * kPrefillGateUpWaves, 0, s>>>(a);
     else
-      prefill_gemm_kernel<true, 4, 2, 2, 4, 4, B, G><<<grid, 256, 0, s>>>(a);
+      prefill_gemm_kernel<true, 4, 2, 2, 4, 4, B, G, 64><<<grid, 256, 0, s>>>(a);
   });
 }
 
@@ -591,10 +603,10 @@ void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& 
     constexpr bool G = decltype(grouped)::value;
     if (c.d_model % (64 * MOE_PF_DN_NJ) == 0) {
       prefill_gemm_kernel<false, MOE_PF_DN_NJ, kPrefillDownStages, kPrefillDownBlocks, MOE_PF_DN_WN,
-                          kPrefillDownWaves, B, G>
+                          kPrefillDownWaves, B, G, 64>
           <<<dim3(c.d_model / (64 * MOE_PF_DN_NJ), p.max_tiles), 64 * kPrefillDownWaves, 0, s>>>(a);
     } else {
-      prefill_gemm_kernel<false, 2, 2, 2, 2, 4, B, G><<<dim3(c.d_model / 128, p.max_tiles), 256, 0, s>>>(a);
+      prefill_gemm_kernel<false, 2, 2, 2, 2, 4, B, G, 64><<<dim3(c.d_model / 128, p.max_tiles), 256, 0, s>>>(a);
     }
   });
 }
