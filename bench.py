@@ -59,12 +59,30 @@ def log(msg):
 
 
 def source_sha() -> str:
-    """Hash of the kernel sources (counter summaries are valid for one version)."""
+    """Hash of all kernel sources."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".h")):
             with open(os.path.join(CSRC, name), "rb") as fh:
                 h.update(name.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+# Sources that decide what a GEMM family's kernels read and write: the kernel
+# file, its headers, the plan (splits, tile sizes) and the row tiles it is given.
+GEMM_FAMILY_SOURCES = {
+    family: [os.path.join(CSRC, f) for f in (f"{family}.hip", "device_common.h", "plan.h", "regroup.h", "moe_api.hip")]
+    + [os.path.join(ROOT, "include", "moe.h")]
+    for family in ("stream_gemm", "prefill_gemm")
+}
+
+
+def family_sha(family: str) -> str:
+    """Hash of one GEMM family's sources: its counter summaries stay valid while it is unchanged."""
+    h = hashlib.sha256()
+    for path in GEMM_FAMILY_SOURCES[family]:
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -174,7 +192,8 @@ def summarize_pmc(dirs, out_path, copy_dirs=(), copy_bytes=1 << 30, workload="")
                 if v > 0:
                     # a copy reads copy_bytes and writes copy_bytes
                     scale[ctr] = copy_bytes / (v * 1024.0)
-    res = {"workload": workload, "source_sha": source_sha(), "copy_bytes": copy_bytes,
+    res = {"workload": workload, "source_sha": source_sha(),
+           "family_sha": {f: family_sha(f) for f in GEMM_FAMILY_SOURCES}, "copy_bytes": copy_bytes,
            "scale": scale, "kernels": kernels}
     with open(out_path, "w") as fh:
         json.dump(res, fh, indent=1)
@@ -183,12 +202,13 @@ def summarize_pmc(dirs, out_path, copy_dirs=(), copy_bytes=1 << 30, workload="")
 
 def load_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from committed counter summaries, if they
-    were taken on the current kernel sources; else None."""
-    sha = source_sha()
+    were taken on the current sources of its GEMM family; else None."""
+    family = kernel.split("_kernel")[0]
+    sha = family_sha(family)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_pmc.json"))):
         with open(path) as fh:
             data = json.load(fh)
-        if data.get("source_sha") != sha:
+        if data.get("family_sha", {}).get(family) != sha:
             continue
         sc = data.get("scale", {})
         for name, ctr in data.get("kernels", {}).items():

@@ -45,6 +45,10 @@ constexpr int kQGroup = 128;            // k per (s, z) group of the grouped for
 #ifndef MOE_PF_GU_BK4
 #define MOE_PF_GU_BK4 128
 #endif
+// per-row gate/up formats: stages handed over inside the last k-step
+#ifndef MOE_PF_GU_HANDOVER
+#define MOE_PF_GU_HANDOVER 1
+#endif
 #ifndef MOE_PF_DN_STAGES
 #define MOE_PF_DN_STAGES 2
 #endif
@@ -395,16 +399,105 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
       }
     }
   };
+  // Per-row gate/up formats with a 2-stage ring hand the stages over in the
+  // middle of a stage's last k-step instead of at its start.  By then a wave
+  // holds that step's fragments in registers (its A fragments were read during
+  // the step before, its codes at the stage's start), so it waits for the next
+  // stage, passes the barrier -- after which no wave reads the current buffer
+  // again -- issues the copies of the stage after next into that buffer, reads
+  // the next stage's codes and first A fragments, and only then runs the last
+  // step's products: the LDS latency after the barrier hides behind them.
+  auto main_loop_handover = [&](auto ml_tag) {
+    constexpr int ML = decltype(ml_tag)::value;
+    auto read_b = [&](const char* buf, u32x4(&bq)[NJW][kCPR / 2]) {
+#pragma unroll
+      for (int j = 0; j < NJW; ++j) {
+        const int r = wr[j] + l32;
+#pragma unroll
+        for (int c = 0; c < kCPR / 2; ++c)
+          bq[j][c] = *reinterpret_cast<const u32x4*>(buf + kABytes + r * kWRow +
+                                                     16 * spos<kCPR>(r, (kCPR / 2) * hh + c));
+      }
+    };
+    auto read_a = [&](const char* buf, int s, u32x4(&av)[MI]) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = 32 * MI * wm + 32 * i + l32;
+        if (i < ML) av[i] = *reinterpret_cast<const u32x4*>(buf + r * kARow + 16 * spos<kACh>(r, kNS * hh + s));
+      }
+    };
+    auto widen = [&](const u32x4(&bq)[NJW][kCPR / 2], int j, int s) {
+      const uint32_t w0 = bq[j][(BITS / 4) * s / 4][((BITS / 4) * s) % 4];
+      if constexpr (BITS == 4) {
+        return codes_to_bf16(w0);
+      } else {
+        const uint32_t w1 = bq[j][(2 * s + 1) / 4][(2 * s + 1) % 4];
+        return bytes_to_bf16(w0, w1);
+      }
+    };
+    static_assert(kNS % 2 == 0, "the last step's A fragments are in av1, the next stage's first in av0");
+    u32x4 bq[NJW][kCPR / 2], av0[MI], av1[MI];
+    wait_vmem<0>();
+    lds_barrier();
+    if (1 < nst) issue(1);
+    read_b(smem, bq);
+    read_a(smem, 0, av0);
+    for (int st = 0; st < nst; ++st) {
+      const char* buf = smem + (st % 2) * kStage;
+#pragma unroll
+      for (int s = 0; s + 1 < kNS; ++s) {
+        u32x4(&cur)[MI] = (s & 1) ? av1 : av0;
+        u32x4(&nxt)[MI] = (s & 1) ? av0 : av1;
+        read_a(buf, s + 1, nxt);
+#pragma unroll
+        for (int j = 0; j < NJW; ++j) {
+          const u32x4 b = widen(bq, j, s);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            if (i < ML) acc[i][j] = mfma32(cur[i], b, acc[i][j]);
+        }
+      }
+      u32x4 bl[NJW];
+#pragma unroll
+      for (int j = 0; j < NJW; ++j) bl[j] = widen(bq, j, kNS - 1);
+      // Unconditional, so that no control-flow merge makes the compiler wait
+      // for these reads before the products below: after the last stage the
+      // reads take the other buffer's stale contents (unused) and the barrier
+      // is one more that every wave takes.
+      __builtin_amdgcn_sched_barrier(0);  // the earlier steps' products stay before the barrier
+      wait_vmem<0>();  // stage st + 1 (this wave's copies of it)
+      lds_barrier();   // ... and every wave's; no wave reads buffer st % 2 again
+      const char* nb = smem + ((st + 1) % 2) * kStage;
+      read_b(nb, bq);
+      read_a(nb, 0, av0);
+      __builtin_amdgcn_sched_barrier(0);  // all of these reads go out before the products
+#pragma unroll
+      for (int j = 0; j < NJW; ++j)
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          if (i < ML) acc[i][j] = mfma32(av1[i], bl[j], acc[i][j]);
+      // the copies of the stage after next, into the buffer just retired
+      // (issued after the products, so that the reads and products above
+      // stay in one block)
+      if (st + 2 < nst) issue(st + 2);
+    }
+  };
   // exactly one instance runs on every path: each takes part in every barrier
   // (live_mi = 0 -- no row of this wave in the tile -- runs the 1-block one)
+  auto run = [&](auto ml_tag) {
+    if constexpr (GATEUP && !GROUPED && kNBuf == 2 && MOE_PF_GU_HANDOVER)
+      main_loop_handover(ml_tag);
+    else
+      main_loop(ml_tag);
+  };
   if (live_mi >= MI)
-    main_loop(std::integral_constant<int, MI>{});
+    run(std::integral_constant<int, MI>{});
   else if (live_mi == 3)
-    main_loop(std::integral_constant<int, 3>{});
+    run(std::integral_constant<int, 3>{});
   else if (live_mi == 2)
-    main_loop(std::integral_constant<int, 2>{});
+    run(std::integral_constant<int, 2>{});
   else
-    main_loop(std::integral_constant<int, 1>{});
+    run(std::integral_constant<int, 1>{});
 
   // epilogue; accumulator element e of lane l is row 8(e/4) + 4(l/32) + e%4, column l%32.
   // Results go through LDS (the stage ring is free once every wave is past
