@@ -97,15 +97,17 @@ __device__ __forceinline__ void wait_vmem() {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Swizzled position of 16-byte chunk c of a row of NC chunks in a stage
-// buffer (activation rows: 8 or 16 chunks; weight rows: 2, 4 or 8).  Eight
-// consecutive rows -- the lanes of one LDS cycle of a fragment read -- then
-// hit 8 different 16-byte bank groups.
+// buffer (activation rows: 8 or 16 chunks; weight rows: 2, 4 or 8).  A
+// fragment read (ds_read_b128) serves 16 lanes -- 16 consecutive rows -- per
+// LDS cycle, 256 bytes across the 64 banks: 256 / (16 NC) rows share one
+// 256-byte line, so the chunk is XORed with the row's index among the rows
+// that fall on the same bank groups, (row / (16 / NC)) mod NC, and the 16
+// rows hit 16 different 16-byte bank groups.
 template <int NC>
 __device__ __forceinline__ int spos(int row, int c) {
-  if constexpr (NC == 2) return c ^ ((row >> 3) & 1);
-  else if constexpr (NC == 4) return c ^ ((row >> 1) & 3);
-  else if constexpr (NC == 8) return c ^ ((row >> 1) & 7);
-  else return c ^ (row & 7);
+  static_assert(NC == 2 || NC == 4 || NC == 8 || NC == 16, "rows of 2 to 16 chunks");
+  constexpr int kShift = NC == 2 ? 3 : NC == 4 ? 2 : NC == 8 ? 1 : 0;  // log2(16 / NC)
+  return c ^ ((row >> kShift) & (NC - 1));
 }
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
