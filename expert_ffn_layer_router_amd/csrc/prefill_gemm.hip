@@ -6,20 +6,24 @@
 // section 4.3 brings 2048-token chunks); section 3.1: per-expert int4 weights
 // with their own scale and zero-point, dequantised on the load path.
 //
-// A block computes a 128-row tile of one expert's group against 256 weight
-// rows (gate/up: 128 output columns of gate and of up; down: 256 output
-// columns) on v_mfma_f32_32x32x16_bf16.  Its 4 waves are 2 x 2, each owning
-// 64 rows x 128 weight rows (8 accumulators of 32 x 32).  The k range is
-// walked in stages of 64: per stage the activation tile (128 rows x 128 B)
-// and the int4 weight tile (256 rows x 32 B) are copied from global memory
-// straight into LDS (global_load_lds_dwordx4), double-buffered and
-// XOR-swizzled for conflict-free fragment reads.  Both A operands (x, copied
-// by the router's top-k kernel, and h) are stored in the fragment k-order of
-// the codes, so fragments go to the matrix cores as read.  Each lane widens one 32-bit
-// word of codes into a bf16 B fragment (codes_to_bf16); scale and zero-point
-// are applied in the epilogue with precomputed row sums of A (token row sums
-// from the router, h row sums from the gate/up epilogue), which keeps the
-// matrix cores free of the extra row-sum product the decode kernels use.
+// A block computes a 128-row tile of one expert's group against 64 NJ weight
+// rows on v_mfma_f32_32x32x16_bf16.  Gate/up: 8 waves side by side along 512
+// weight rows (256 output columns of gate and of up), one block per compute
+// unit; down: 4 waves along 256 weight rows (256 output columns), two blocks
+// per compute unit.  Each wave owns 128 rows x 64 weight rows (8 accumulators
+// of 32 x 32), so every widened weight fragment feeds 4 products and is
+// widened by one wave only.  The k range is walked in stages (128 k for the
+// int4 gate/up blocks, 64 k otherwise): per stage the activation tile (128
+// rows) and the weight-code tile are copied from global memory straight into
+// LDS (global_load_lds_dwordx4) through a 2-stage ring, with a chunk swizzle
+// that keeps the fragment reads free of bank conflicts.  Both A operands (x,
+// copied by the router's top-k kernel, and h) are stored in the fragment
+// k-order of the codes, so fragments go to the matrix cores as read.  Each
+// lane widens one 32-bit word of codes into a bf16 B fragment
+// (codes_to_bf16); scale and zero-point are applied in the epilogue with
+// precomputed row sums of A (token row sums from the router, h row sums from
+// the gate/up epilogue), which keeps the matrix cores free of the extra
+// row-sum product the decode kernels use.
 #include <type_traits>
 
 #include "device_common.h"
