@@ -5,14 +5,17 @@ A step is one full layer forward (router top-k, regroup, int4 gate/up GEMM
 with SwiGLU, down GEMM, combine) over one batch of the workload.  Prints ONE
 JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--config mixtral_decode] [--mode graph|eager]
+    python bench.py [--steps K] [--warmup W] [--config mixtral_decode] [--sub-configs auto|none|a,b]
 
 Inputs are seeded synthetic layers (synth package) resident in HBM before
-timing starts.  By default one HIP graph replays 32 layers back to back, as
-a Mixtral-8x7B decode step would, each layer with its own copy of the weight
-pool, so that a step never finds the previous step's weights in the 256 MB
-MALL (a model's successive layers have different weights); the graph's own
-launch is then paid once per 32 layer steps.
+timing starts.  The steps run as replays of one HIP graph that holds several
+consecutive layers back to back, as a model's decode-step graph would, each
+layer with its own copy of the weight pool, so that a step never finds the
+previous step's weights in the 256 MB MALL (a model's successive layers have
+different weights).  The graph's length divides K, so the timed region is
+exactly K layer steps; the W warm-up steps are whole replays plus single
+layers.  The headline `value` is the --config workload; the line's `configs`
+holds the same record for each of the five BASELINE workloads.
 
 Extra modes for counter runs:
     --copy-calibration   time a plain 1 GiB device copy (scale for FETCH/WRITE_SIZE)
@@ -119,6 +122,10 @@ def cpu_baseline(case, budget_s=15.0):
         threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    try:
+        available = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        available = os.cpu_count() or 1
     shape, w = case.shape, case.weights
     kw = {a: getattr(w, a) for a in w.ARRAYS}
     n_tok = min(shape.T, 64)
@@ -150,9 +157,10 @@ def cpu_baseline(case, budget_s=15.0):
     except OSError:
         pass
     sample = (f"{n_tok} of {shape.T} tokens of the same workload, full forward incl. dequant of the "
-              f"experts they use, median of {len(times)} runs; host CPU: {cpu}")
-    res = {"value": n_tok / med, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample,
-           "seconds_per_run": med}
+              f"experts they use, median of {len(times)} runs; BLAS on {threads} threads of the "
+              f"{available} cores in the process's affinity mask; host CPU: {cpu}")
+    res = {"value": n_tok / med, "unit": "tokens/s", "cores": threads, "host_cores_available": available,
+           "kind": "oracle", "sample": sample, "seconds_per_run": med}
     if single is not None:
         res["single_thread"] = {"value": n_tok / single, "unit": "tokens/s", "seconds_per_run": single}
     return res
@@ -232,23 +240,29 @@ def copy_calibration(gib=1.0, reps=5):
 
 # --------------------------------------------------------------------------- main bench
 def achievable_peaks(shape, torch, reps=10):
-    """What plain library code reaches on this GPU, as a second yardstick next
-    to the vendor peaks: a 2 GiB device copy (read + write bytes / time, torch's
-    copy kernel) and a dense bf16 GEMM shaped like the gate/up product of the
-    workload's rows (hipBLASLt through torch.matmul)."""
-    n = 1 << 31
-    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
+    """What simple code reaches on this GPU, a second yardstick next to the
+    vendor peaks: a read-only stream of 4 GiB through the library's read probe
+    (the best of three grid sizes; bytes read / time), and a dense bf16 GEMM
+    shaped like the gate/up product of the workload's rows (hipBLASLt through
+    torch.matmul)."""
+    from expert_ffn_layer_router_amd import hbm_read_probe
+    n = 4 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(0x5A)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    ev1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * n * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
-    del src, dst
+    read_gbs, best_blocks = 0.0, 0
+    for blocks in (1024, 2048, 4096):
+        hbm_read_probe(buf, sink, blocks)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            hbm_read_probe(buf, sink, blocks)
+        ev1.record()
+        torch.cuda.synchronize()
+        gbs = n * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+        if gbs > read_gbs:
+            read_gbs, best_blocks = gbs, blocks
+    del buf, sink
     M = max(256, -(-shape.T * (shape.top_k + shape.num_shared) // 256) * 256)
     N, K = 2 * shape.d_ff, shape.d_model
     a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
@@ -261,9 +275,10 @@ def achievable_peaks(shape, torch, reps=10):
     ev1.record()
     torch.cuda.synchronize()
     gemm_tflops = 2 * M * N * K * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
-    return {"hbm_copy_gbs": copy_gbs, "bf16_gemm_tflops": gemm_tflops,
+    return {"hbm_read_gbs": read_gbs, "hbm_read_blocks": best_blocks, "bf16_gemm_tflops": gemm_tflops,
             "bf16_gemm_shape": [M, N, K],
-            "how": "2 GiB torch device copy (read+write bytes); torch.matmul bf16 (hipBLASLt) of the gate/up shape"}
+            "how": "4 GiB read-only stream (moe_hbm_read_probe, 256-thread blocks, best grid); "
+                   "torch.matmul bf16 (hipBLASLt) of the gate/up shape"}
 
 
 def step_percentiles(step, stream, torch, n=60):
@@ -277,6 +292,193 @@ def step_percentiles(step, stream, torch, n=60):
     stream.synchronize()
     ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
     return {"p10": ts[n // 10], "p50": ts[n // 2], "p90": ts[(9 * n) // 10], "n": n}
+
+
+def graph_length(steps: int, max_layers: int = 32) -> int:
+    """Layers per replayed graph: a divisor of `steps`, so that the timed
+    region is whole replays of one graph, with at least two replays when that
+    leaves graphs of 4 or more layers."""
+    if steps <= 3:
+        return max(1, steps)
+    cap = min(max_layers, steps // 2)
+    n = max(d for d in range(1, cap + 1) if steps % d == 0)
+    if n < 4 and steps <= max_layers:
+        n = steps
+    return n
+
+
+def build_layer_graph(layers, pools, outs, x, rw, rb, st, ws, stream, torch):
+    """One HIP graph holding len(layers) layer forwards back to back: layer i
+    with its own handle, weight pool pools[i % len(pools)] and output outs[i],
+    all reading the same hidden state and sharing one workspace -- a model's
+    decode-step graph, each layer with its own weights.  The handles run once
+    eagerly first (outside the capture)."""
+    def run_all():
+        for i, L in enumerate(layers):
+            L.forward(x, rw, rb, st, pools[i % len(pools)], out=outs[i], workspace=ws, stream=stream)
+    run_all()
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        run_all()
+    stream.synchronize()
+    return g
+
+
+# BASELINE targets at layer level: decode shapes >= 70 % of HBM peak, prefill >= 50 % of bf16 peak
+LAYER_TARGET_FRAC = {"hbm": 0.70, "mfma": 0.50}
+HEADLINE_CONFIGS = ("mixtral_decode", "mixtral_prefill", "phi35_skew", "fine_decode", "fine_prefill")
+
+
+def run_workload(name, steps, warmup, torch, *, mode="layers", model_layers=32, stage_timing=True,
+                 pool_budget=60e9, log_prefix=""):
+    """Times `steps` layer steps (after `warmup` untimed ones) of workload
+    `name` and returns its record plus the objects the other bench legs reuse."""
+    import synth
+    from expert_ffn_layer_router_amd import DeviceWeights, MoeLayer, to_device
+
+    case = synth.make_case(name)
+    shape, w = case.shape, case.weights
+    T = shape.T
+    log(f"{log_prefix}workload {name}: T={T} d={shape.d_model} d_ff={shape.d_ff} E={shape.num_experts} "
+        f"k={shape.top_k} shared={shape.num_shared} slots={shape.num_slots}")
+    x = to_device(case.hidden).view(torch.bfloat16)
+    rw = to_device(w.router_w)
+    rb = None if w.router_b is None else to_device(w.router_b)
+    st = to_device(w.slot_table)
+
+    def new_layer():
+        return MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T,
+                        num_shared=shape.num_shared, weight_bits=shape.bits, group_size=shape.group)
+
+    probe = new_layer()
+    ws = probe.new_workspace(T)
+    pools = [DeviceWeights.upload(w)]
+    out0 = torch.empty((T, shape.d_model), dtype=torch.bfloat16, device="cuda")
+    probe.forward(x, rw, rb, st, pools[0], out=out0, workspace=ws)
+    torch.cuda.synchronize()
+    counts = probe.routing(ws, T)["counts"].cpu().numpy()
+    work = algorithmic_work(shape, counts)
+    plan_fused = T <= STREAM_MAX_TOKENS
+
+    nlay = graph_length(steps, model_layers) if mode == "layers" else 1
+    pool_bytes = w.nbytes()
+    rot = max(1, min(nlay if mode == "layers" else model_layers, int(pool_budget // max(1, pool_bytes))))
+    if rot < 2:
+        log(f"{log_prefix}only one weight-pool copy fits: steps may find weights in the MALL")
+    while len(pools) < rot:
+        pools.append(pools[0].clone())
+    log(f"{log_prefix}{work['active']} active experts, {work['layer']['bytes'] / 1e6:.1f} MB algorithmic per "
+        f"step, {rot} weight-pool copies of {pool_bytes / 1e6:.1f} MB")
+    stream = torch.cuda.Stream()
+
+    if mode == "layers":
+        layers = [new_layer() for _ in range(nlay)]
+        outs = [torch.empty((T, shape.d_model), dtype=torch.bfloat16, device="cuda") for _ in range(nlay)]
+        graph = build_layer_graph(layers, pools, outs, x, rw, rb, st, ws, stream, torch)
+        with torch.cuda.stream(stream):
+            graph.replay()  # set-up: the graph's first launch uploads it
+        stream.synchronize()
+    else:
+        layers = [probe]
+        outs = [out0]
+        graph = None
+
+    def eager(i):
+        L = layers[i % len(layers)]
+        L.forward(x, rw, rb, st, pools[i % rot], out=outs[i % len(outs)], workspace=ws, stream=stream)
+
+    # warm-up: exactly `warmup` layer steps (whole replays, then single layers)
+    with torch.cuda.stream(stream):
+        if mode == "layers":
+            for _ in range(warmup // nlay):
+                graph.replay()
+            for i in range(warmup % nlay):
+                eager(i)
+        else:
+            for i in range(warmup):
+                eager(i)
+    stream.synchronize()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` layer steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        if mode == "layers":
+            for _ in range(steps // nlay):
+                graph.replay()
+        else:
+            for i in range(steps):
+                eager(i)
+        ev1.record(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    us_per_step = 1e6 * wall / steps
+    log(f"{log_prefix}{mode}: {us_per_step:.1f} us/step wall, {ev_ms / steps * 1e3:.1f} us/step events "
+        f"({steps} steps, {'graphs of %d layers' % nlay if mode == 'layers' else 'eager'})")
+
+    # kernel time: HIP events the library records between its stages, on the
+    # kernels' own stream, over `steps` eager layer steps of the same layers
+    stage_us = {}
+    if stage_timing:
+        for L in layers:
+            L.set_stage_timing(-(-steps // len(layers)))
+        with torch.cuda.stream(stream):
+            for i in range(steps):
+                eager(i)
+        stream.synchronize()
+        stage_sum, n_fw = {}, 0
+        for L in layers:
+            ms, n = L.stage_times()
+            n_fw += n
+            for key, v in ms.items():
+                stage_sum[key] = stage_sum.get(key, 0.0) + v
+            L.set_stage_timing(0)
+        # few tokens: the regroup runs inside the router kernel and the combine
+        # inside the down kernel -- no kernel of their own to time
+        fused = ("regroup", "combine") if plan_fused else ()
+        stage_us = {key: 1e3 * v / max(1, n_fw) for key, v in stage_sum.items() if key not in fused}
+        log(f"{log_prefix}stage us: " + ", ".join(f"{key} {v:.1f}" for key, v in stage_us.items()))
+
+    bound = DECODE_BOUND.get(name, "hbm")
+    layer_s = us_per_step * 1e-6
+    lay = work["layer"]
+    rec = {"T": T, "tokens_per_s": T * steps / wall, "us_per_step": us_per_step, "steps": steps,
+           "warmup": warmup, "bound": bound,
+           "timing": (f"{steps // nlay} replays of a HIP graph of {nlay} layers (own weights each)"
+                      if mode == "layers" else "eager launches"),
+           "weight_pool_copies": rot, "active_experts": work["active"],
+           "layer": {"algorithmic_bytes": lay["bytes"], "algorithmic_flops": lay["flops"],
+                     "hbm_gbs": lay["bytes"] / layer_s / 1e9, "hbm_frac": lay["bytes"] / layer_s / 1e9 / HBM_PEAK_GBS,
+                     "mfma_tflops": lay["flops"] / layer_s / 1e12,
+                     "mfma_frac": lay["flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS},
+           "stage_us": stage_us}
+    rec["layer"]["frac"] = rec["layer"]["hbm_frac" if bound == "hbm" else "mfma_frac"]
+    rec["layer"]["target_frac"] = LAYER_TARGET_FRAC[bound]
+    rec["layer"]["meets_target"] = rec["layer"]["frac"] >= LAYER_TARGET_FRAC[bound]
+    if stage_us:
+        dom = max(("gate_up", "down"), key=lambda s_: stage_us[s_])
+        dur_s = stage_us[dom] * 1e-6
+        if bound == "hbm":
+            achieved = work[dom]["bytes"] / dur_s / 1e9
+            roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS}
+        else:
+            achieved = work[dom]["flops"] / dur_s / 1e12
+            roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / BF16_PEAK_TFLOPS}
+        roof["traffic"] = load_traffic(name, kernel_of_stage(dom, T))
+        roof.update({"kernel": kernel_of_stage(dom, T), "kernel_us": stage_us[dom],
+                     "algorithmic_bytes": work[dom]["bytes"], "algorithmic_flops": work[dom]["flops"]})
+        rec["roofline"] = roof
+    ctx = dict(case=case, shape=shape, layers=layers, pools=pools, stream=stream, eager=eager, graph=graph,
+               nlay=nlay, ev_ms=ev_ms)
+    return rec, ctx
 
 
 def run_refill(args, shape, w, pools, layer, step, stream, torch):
@@ -342,19 +544,20 @@ def run_refill(args, shape, w, pools, layer, step, stream, torch):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="mixtral_decode")
-    ap.add_argument("--mode", choices=["layers", "graph", "eager"], default="layers",
-                    help="layers: one HIP graph replays the rotated layers back to back (a model's decode-step "
-                         "graph); graph: one graph per layer step; eager: plain launches")
-    ap.add_argument("--rotations", type=int, default=0,
-                    help="weight-pool copies = layers in the layers-mode graph (0: --model-layers, and at least "
-                         "enough to defeat the MALL)")
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--config", default="mixtral_decode", help="the workload of the headline value")
+    ap.add_argument("--sub-configs", default="auto",
+                    help="comma-separated workloads also measured into the line's `configs` ('auto': the five "
+                         "BASELINE workloads; 'none': only --config)")
+    ap.add_argument("--sub-steps", type=int, default=64, help="timed layer steps per sub-workload")
+    ap.add_argument("--mode", choices=["layers", "eager"], default="layers",
+                    help="layers: HIP graphs of consecutive layers (own weights each) replayed, as a model's "
+                         "decode-step graph; eager: plain launches")
     ap.add_argument("--model-layers", type=int, default=32,
-                    help="MoE layers of the model's decode-step graph (Mixtral-8x7B: 32), each with its own weights")
+                    help="most layers per graph (Mixtral-8x7B has 32 MoE layers), each with its own weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-peaks", action="store_true", help="skip the copy / library-GEMM yardsticks")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the read-stream / library-GEMM yardsticks")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--refill", action="store_true",
@@ -374,12 +577,11 @@ def main(argv=None):
         print(f"bench.py measures one GPU only: this layer is built and measured on a single MI355X "
               f"(--gpus {args.gpus} / WORLD_SIZE {world} is not supported)", file=sys.stderr)
         return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
 
-    import numpy as np
     import torch
-
-    import synth
-    from expert_ffn_layer_router_amd import DeviceWeights, MoeLayer, to_device
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -389,169 +591,57 @@ def main(argv=None):
         return 0
 
     torch.cuda.set_device(0)
-    case = synth.make_case(args.config)
-    shape, w = case.shape, case.weights
-    log(f"workload {args.config}: T={shape.T} d={shape.d_model} d_ff={shape.d_ff} E={shape.num_experts} "
-        f"k={shape.top_k} shared={shape.num_shared} slots={shape.num_slots}")
-
-    # routing of this batch (for the work accounting)
-    pool_bytes = w.nbytes()
-    T = shape.T
-    x = to_device(case.hidden).view(torch.bfloat16)
-    rw = to_device(w.router_w)
-    rb = None if w.router_b is None else to_device(w.router_b)
-    st = to_device(w.slot_table)
-    probe = MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T,
-                     num_shared=shape.num_shared, weight_bits=shape.bits, group_size=shape.group)
-    ws = probe.new_workspace(T)
-    out = torch.empty((T, shape.d_model), dtype=torch.bfloat16, device="cuda")
-
-    pools = [DeviceWeights.upload(w)]
-    probe.forward(x, rw, rb, st, pools[0], out=out, workspace=ws)
-    torch.cuda.synchronize()
-    counts = probe.routing(ws, T)["counts"].cpu().numpy()
-    work = algorithmic_work(shape, counts)
-    active_bytes = work["layer"]["bytes"]
-    rot = args.rotations or max(2, args.model_layers, -(-int(1.5 * MALL_BYTES) // max(1, active_bytes)) + 1)
-    rot = min(rot, max(1, int(60e9 // max(1, pool_bytes))))
-    for _ in range(rot - 1):
-        pools.append(DeviceWeights.upload(w))
-    log(f"{work['active']} active experts, {active_bytes / 1e6:.1f} MB algorithmic per step, "
-        f"{rot} weight-pool copies of {pool_bytes / 1e6:.1f} MB")
-
-    layers = [MoeLayer(shape.d_model, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T,
-                       num_shared=shape.num_shared, weight_bits=shape.bits, group_size=shape.group)
-              for _ in range(rot)]
-    stream = torch.cuda.Stream()
-    multi = None
-    if args.mode == "graph":
-        with torch.cuda.stream(stream):
-            for L, p in zip(layers, pools):
-                L.capture(x, rw, rb, st, p, out, ws, stream)
-        stream.synchronize()
-    elif args.mode == "layers":
-        # one graph = the `rot` layers back to back, each with its own weights
-        for i in range(rot):  # warm the handles outside capture
-            layers[i].forward(x, rw, rb, st, pools[i], out=out, workspace=ws, stream=stream)
-        stream.synchronize()
-        multi = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(multi, stream=stream):
-            for L, p in zip(layers, pools):
-                L.forward(x, rw, rb, st, p, out=out, workspace=ws, stream=stream)
-        stream.synchronize()
-        args.steps = -(-args.steps // rot) * rot
-        args.warmup = -(-args.warmup // rot) * rot
-
-    def step(i):
-        if args.mode == "graph":
-            layers[i % rot].replay(stream)
-        elif args.mode == "layers":
-            if i % rot == 0:
-                multi.replay()
-        else:
-            layers[i % rot].forward(x, rw, rb, st, pools[i % rot], out=out, workspace=ws, stream=stream)
-
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            step(i)
-    stream.synchronize()
-    torch.cuda.synchronize()
-
+    rec, ctx = run_workload(args.config, args.steps, args.warmup, torch, mode=args.mode,
+                            model_layers=args.model_layers)
+    shape, stream = ctx["shape"], ctx["stream"]
     if args.refill:
-        return run_refill(args, shape, w, pools, layers[0], step, stream, torch)
+        return run_refill(args, shape, ctx["case"].weights, ctx["pools"], ctx["layers"][0], ctx["eager"], stream,
+                          torch)
 
-    # timed region: K whole-layer steps
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        for i in range(args.steps):
-            step(i)
-        ev1.record(stream)
-    stream.synchronize()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = ev0.elapsed_time(ev1)
-    ms_per_step = 1e3 * wall / args.steps
-    value = T * args.steps / wall
-    log(f"{args.mode}: {ms_per_step * 1e3:.1f} us/step wall, {ev_ms / args.steps * 1e3:.1f} us/step events")
-
-    # kernel timing: HIP events recorded by the library between stages, on the
-    # stream the kernels run on (eager launches of the same steps)
-    for L in layers:
-        L.set_stage_timing(args.steps)
-    with torch.cuda.stream(stream):
-        for i in range(args.steps):
-            layers[i % rot].forward(x, rw, rb, st, pools[i % rot], out=out, workspace=ws, stream=stream)
-    stream.synchronize()
-    stage_sum = {}
-    n_fw = 0
-    for L in layers:
-        ms, n = L.stage_times()
-        n_fw += n
-        for key, v in ms.items():
-            stage_sum[key] = stage_sum.get(key, 0.0) + v
-        L.set_stage_timing(0)
-    stage_us = {key: 1e3 * v / max(1, n_fw) for key, v in stage_sum.items()}
-    log("stage us: " + ", ".join(f"{key} {v:.1f}" for key, v in stage_us.items()))
-
-    bound = DECODE_BOUND.get(args.config, "hbm")
-    dom = max(("gate_up", "down"), key=lambda s_: stage_us[s_])
-    dur_s = stage_us[dom] * 1e-6
-    if bound == "hbm":
-        achieved = work[dom]["bytes"] / dur_s / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS}
-    else:
-        achieved = work[dom]["flops"] / dur_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / BF16_PEAK_TFLOPS}
-    roof["kernel"] = kernel_of_stage(dom, T)
-    roof["kernel_us"] = stage_us[dom]
-    roof["algorithmic_bytes"] = work[dom]["bytes"]
-    roof["algorithmic_flops"] = work[dom]["flops"]
-    roof["traffic"] = load_traffic(args.config, kernel_of_stage(dom, T))
-
-    # single-step latency spread, and the yardsticks plain library code reaches
-    if args.mode == "layers":
-        per = step_percentiles(lambda i: step(i * rot), stream, torch)
-        per = {key: (v / rot if key != "n" else v) for key, v in per.items()}
-    else:
-        per = step_percentiles(step, stream, torch)
+    # single-step latency spread (one layer per replay of a one-layer graph would
+    # add a graph launch per step, so these are eager single layers)
+    per = step_percentiles(ctx["eager"], stream, torch)
     peaks = None
+    roof = dict(rec["roofline"])
     if not args.no_peaks:
         peaks = achievable_peaks(shape, torch)
-        ref = peaks["hbm_copy_gbs"] if roof["bound"] == "hbm" else peaks["bf16_gemm_tflops"]
+        ref = peaks["hbm_read_gbs"] if roof["bound"] == "hbm" else peaks["bf16_gemm_tflops"]
         roof["frac_of_achievable"] = roof["achieved"] / ref
-        log(f"achievable: copy {peaks['hbm_copy_gbs']:.0f} GB/s, bf16 GEMM {peaks['bf16_gemm_tflops']:.0f} TFLOP/s")
+        log(f"achievable: read {peaks['hbm_read_gbs']:.0f} GB/s, bf16 GEMM {peaks['bf16_gemm_tflops']:.0f} TFLOP/s")
 
-    layer_s = ms_per_step * 1e-3
+    configs = {args.config: rec}
+    subs = [c for c in (HEADLINE_CONFIGS if args.sub_configs == "auto" else
+                        ([] if args.sub_configs == "none" else args.sub_configs.split(","))) if c and c != args.config]
+    del ctx
+    for name in subs:
+        torch.cuda.empty_cache()
+        sub, sctx = run_workload(name, args.sub_steps, graph_length(args.sub_steps, args.model_layers), torch,
+                                 mode=args.mode, model_layers=args.model_layers, log_prefix="  ")
+        del sctx
+        configs[name] = sub
+
     result = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": args.config, "T": T, "d_model": shape.d_model, "d_ff": shape.d_ff,
+        "metric": METRIC, "value": rec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": rec["us_per_step"] * 1e-3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.config, "T": shape.T, "d_model": shape.d_model, "d_ff": shape.d_ff,
                    "num_experts": shape.num_experts, "top_k": shape.top_k, "num_shared": shape.num_shared,
                    "num_slots": shape.num_slots,
                    "weights": (f"{'int4' if shape.bits == 4 else '8-bit'} codes + fp16 scale/zero-point per "
                                + ("output row" if not shape.group else f"output row and {shape.group}-input group")),
-                   "mode": {"layers": f"HIP graph of {rot} consecutive layers (own weights each), replayed",
-                            "graph": "one HIP graph per layer step", "eager": "eager launches"}[args.mode],
-                   "weight_pool_copies": rot, "parallelism": "single GPU"},
+                   "timing": rec["timing"], "weight_pool_copies": rec["weight_pool_copies"],
+                   "parallelism": "single GPU"},
         "roofline": roof,
-        "layer": {"algorithmic_bytes": work["layer"]["bytes"], "algorithmic_flops": work["layer"]["flops"],
-                  "hbm_gbs": work["layer"]["bytes"] / layer_s / 1e9,
-                  "mfma_frac": work["layer"]["flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS,
-                  "active_experts": work["active"], "stage_us": stage_us,
-                  "event_us_per_step": 1e3 * ev_ms / args.steps},
+        "layer": dict(rec["layer"], active_experts=rec["active_experts"], stage_us=rec["stage_us"]),
+        "configs": configs,
         "step_us": per,
         "achievable": peaks,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget_s)
+        import synth
+        result["cpu_baseline"] = cpu_baseline(synth.make_case(args.config), args.cpu_budget_s)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -6,4 +6,4 @@ include/moe.h; this package is its thin Python binding.
 """
 
 from ._lib import MoeError, load, MOE_FLAG_BAD_SLOT  # noqa: F401
-from .layer import DeviceWeights, ExpertCache, HostExpert, MoeLayer, to_device  # noqa: F401
+from .layer import DeviceWeights, ExpertCache, HostExpert, MoeLayer, hbm_read_probe, to_device  # noqa: F401

@@ -3,12 +3,14 @@
 from __future__ import annotations
 
 import ctypes
+import glob
 import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_hip.so")
-HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+HEADERS = sorted(glob.glob(os.path.join(INCLUDE, "*.h")))
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = 1
@@ -48,11 +50,14 @@ _lib = None
 
 
 def header_functions() -> list:
-    """Names of the functions include/moe.h declares."""
-    with open(HEADER) as fh:
-        text = fh.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for path in HEADERS:
+        with open(path) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def load():
@@ -87,6 +92,7 @@ def load():
         "moe_device_flags": (c_int, [vp, vp, i32, vp, ctypes.POINTER(ctypes.c_uint32)]),
         "moe_set_stage_timing": (c_int, [vp, i32]),
         "moe_stage_times": (c_int, [vp, ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]),
+        "moe_hbm_read_probe": (c_int, [vp, sz, vp, i32, vp]),
         "moe_status_string": (ctypes.c_char_p, [c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
     }

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_hip.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["router.hip", "permute.hip", "stream_gemm.hip", "prefill_gemm.hip", "combine.hip", "moe_api.hip",
-           "expert_cache.hip"]
+           "expert_cache.hip", "measure.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -76,6 +76,8 @@ struct moe_layer {
   moe_config ecfg{};
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  int graph_device = -1;  // the device current when the graph was captured
+  int graph_T = 0;        // its token count
   // stage timing: (MOE_NUM_STAGES + 1) events per recorded forward
   std::vector<hipEvent_t> events;
   int timing_capacity = 0;
@@ -361,9 +363,13 @@ MOE_EXPORT moe_status moe_graph_capture(moe_handle h, int32_t T, const uint16_t*
   if (st != MOE_OK) return st;
   if (!stream) return fail(MOE_ERR_INVALID_ARG, "graph capture needs a non-null stream");
   if (T == 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "graph capture needs T > 0");
-  drop_graph(h);
+  int device = -1;
+  hipError_t err = hipGetDevice(&device);
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(err));
+  // The new graph replaces the held one only once it is instantiated: a
+  // failed capture leaves the handle's earlier graph (if any) in place.
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  err = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
   if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(err));
   const moe_status est = enqueue(h, p, hidden, router_w, router_bias, slot_table, w, out, workspace, s, true);
   hipGraph_t graph = nullptr;
@@ -372,15 +378,21 @@ MOE_EXPORT moe_status moe_graph_capture(moe_handle h, int32_t T, const uint16_t*
     if (graph) (void)hipGraphDestroy(graph);
     return est;
   }
-  if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(err));
+  if (err != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return fail(MOE_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(err));
+  }
   hipGraphExec_t exec = nullptr;
   err = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
   if (err != hipSuccess) {
     (void)hipGraphDestroy(graph);
     return fail(MOE_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(err));
   }
+  drop_graph(h);
   h->graph = graph;
   h->exec = exec;
+  h->graph_device = device;
+  h->graph_T = T;
   return MOE_OK;
 }
 
@@ -388,7 +400,14 @@ MOE_EXPORT moe_status moe_graph_launch(moe_handle h, moe_stream stream) {
   moe_status st = check_handle(h);
   if (st != MOE_OK) return st;
   if (!h->exec) return fail(MOE_ERR_BAD_STATE, "no captured graph");
-  const hipError_t err = hipGraphLaunch(h->exec, static_cast<hipStream_t>(stream));
+  int device = -1;
+  hipError_t err = hipGetDevice(&device);
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(err));
+  // the graph's kernels and pointers belong to the device it was captured on
+  if (device != h->graph_device)
+    return fail(MOE_ERR_BAD_STATE, "graph (T=%d) was captured on device %d, device %d is current", h->graph_T,
+                h->graph_device, device);
+  err = hipGraphLaunch(h->exec, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGraphLaunch: %s", hipGetErrorString(err));
   return MOE_OK;
 }
@@ -469,3 +488,4 @@ MOE_EXPORT const char* moe_status_string(moe_status s) {
 }
 
 MOE_EXPORT const char* moe_last_error(void) { return g_last_error.c_str(); }
+

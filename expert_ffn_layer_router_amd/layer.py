@@ -46,6 +46,20 @@ class DeviceWeights:
     def struct(self) -> _lib.MoeWeights:
         return _lib.MoeWeights(**{f: _ptr(self.tensors[f]) for f in WEIGHT_FIELDS})
 
+    def clone(self) -> "DeviceWeights":
+        """A second copy of the pool in device memory (device-to-device copies)."""
+        return DeviceWeights({f: t.clone() for f, t in self.tensors.items()})
+
+
+def hbm_read_probe(buf, sink, blocks: int = 2048, stream=None) -> None:
+    """moe_hbm_read_probe: one read of the device tensor `buf`, XOR-folded into
+    the int32 device tensor `sink` (measurement yardstick)."""
+    torch = _torch()
+    lib = _lib.load()
+    s = torch.cuda.current_stream() if stream is None else stream
+    _lib.check(lib.moe_hbm_read_probe(_ptr(buf), int(buf.numel() * buf.element_size()), _ptr(sink), int(blocks),
+                                      ctypes.c_void_p(int(s.cuda_stream))))
+
 
 class MoeLayer:
     """One layer shape.  Mirrors moe_create / moe_forward / moe_routing_view /

@@ -59,3 +59,18 @@ def test_family_hash_follows_its_sources(tmp_path, monkeypatch):
     before = bench.family_sha("stream_gemm")
     (tmp_path / "h.h").write_text("h.h changed")
     assert bench.family_sha("stream_gemm") != before
+
+
+def test_graph_length_divides_the_step_count():
+    """The timed region is whole replays of one graph: its length divides the
+    step count, with at least two replays when that leaves 4 or more layers
+    per graph, and never more layers than the model has."""
+    for steps in list(range(1, 70)) + [96, 97, 100, 128, 256, 1000]:
+        n = bench.graph_length(steps, 32)
+        assert steps % n == 0 and 1 <= n <= max(32, 1)
+        if steps >= 8 and any(steps % q == 0 for q in range(4, min(32, steps // 2) + 1)):
+            assert steps // n >= 2
+    assert bench.graph_length(20) == 10
+    assert bench.graph_length(256) == 32
+    assert bench.graph_length(5) == 5
+    assert bench.graph_length(7) == 7

@@ -209,21 +209,31 @@ def test_graph_replay_matches_eager_and_reads_inputs_at_replay(name):
     say(f"{name}: capture, T={T}")
     with torch.cuda.stream(stream):
         gl.layer.capture(xb, gl.router_w, gl.router_b, table, gl.dw, out, ws, stream)
+    from gpu_util import bf16_bits_to_f64
+    ref1 = _oracle(case)
     for rep in range(3):
         with torch.cuda.stream(stream):
             gl.layer.replay(stream)
         stream.synchronize()
         got = out.cpu().view(torch.int16).numpy()
         np.testing.assert_array_equal(got, e1["out_bits"], err_msg=f"replay {rep}")
+        # the replay against the oracle itself: routing bit-exact, out within 2e-2
+        check_routing({k: v.cpu().numpy() for k, v in gl.layer.routing(ws, T).items()}, ref1)
+        assert_out_close(bf16_bits_to_f64(out), ref1["out"], what=f"replay {rep}")
         _ = (xb.float() * 2).sum().item()             # eager work between replays
     # new hidden states and a rewritten slot table, read at replay
     xb.copy_(gl.hidden(x2))
     table.copy_(gl.to_device(copy_table))
     torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        gl.layer.replay(stream)
-    stream.synchronize()
-    np.testing.assert_array_equal(out.cpu().view(torch.int16).numpy(), e2["out_bits"])
+    ref2 = _oracle(case, hidden=x2, **{f: arrays[f] for f in arrays}, slot_table=copy_table)
+    for rep in range(2):
+        with torch.cuda.stream(stream):
+            gl.layer.replay(stream)
+        stream.synchronize()
+        np.testing.assert_array_equal(out.cpu().view(torch.int16).numpy(), e2["out_bits"], err_msg=f"rep {rep}")
+        check_routing({k: v.cpu().numpy() for k, v in gl.layer.routing(ws, T).items()}, ref2)
+        assert_out_close(bf16_bits_to_f64(out), ref2["out"], what=f"rewritten inputs, replay {rep}")
+        _ = (xb.float() * 3).sum().item()
 
 
 def test_zero_tokens_is_a_noop():
@@ -327,3 +337,66 @@ def test_one_hot_expert_takes_every_token(T):
     assert np.all(ref["topk_idx"][:, 0] == 5) and ref["counts"][5] == T
     check_routing(res, ref)
     assert_out_close(res["out"], ref["out"])
+
+
+def test_layers_graph_at_the_benchmarked_decode_shape_matches_the_oracle():
+    """The graph bench.py times: several Mixtral-shaped decode layers (T = 16,
+    d = 4096, d_ff = 14336, E = 8, top-2) back to back in one HIP graph, each
+    with its own handle, its own copy of the weight pool and its own output,
+    one shared workspace -- built by bench.py's own graph builder.  Every
+    layer's output is checked against the oracle on every replay, and after a
+    pool copy is rewritten in place (two experts' weights exchanged) only the
+    layer reading that copy changes, to the oracle's new result."""
+    torch = require_gpu()
+    import bench
+    from expert_ffn_layer_router_amd import DeviceWeights, MoeLayer, to_device
+    from gpu_util import bf16_bits_to_f64
+    case = synth.make_case("mixtral_decode")
+    shape, w = case.shape, case.weights
+    T, d, nl = shape.T, shape.d_model, 3
+    say(f"mixtral_decode: {nl}-layer graph, T={T}")
+    x = to_device(case.hidden).view(torch.bfloat16)
+    rw, st = to_device(w.router_w), to_device(w.slot_table)
+    pools = [DeviceWeights.upload(w)]
+    pools += [pools[0].clone() for _ in range(nl - 1)]
+    layers = [MoeLayer(d, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T) for _ in range(nl)]
+    outs = [torch.empty((T, d), dtype=torch.bfloat16, device="cuda") for _ in range(nl)]
+    ws = layers[0].new_workspace(T)
+    stream = torch.cuda.Stream()
+    graph = bench.build_layer_graph(layers, pools, outs, x, rw, None, st, ws, stream, torch)
+    ref = _oracle(case)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        stream.synchronize()
+        for i, o in enumerate(outs):
+            assert_out_close(bf16_bits_to_f64(o), ref["out"], what=f"layer {i}, replay {rep}")
+        check_routing({k: v.cpu().numpy() for k, v in layers[-1].routing(ws, T).items()}, ref)
+        _ = (x.float() * 2).sum().item()             # eager work between replays
+    # pool copy 1 now holds another layer: experts 0 and 1 exchange weights
+    s0, s1 = int(w.slot_table[0]), int(w.slot_table[1])
+    for f, t in pools[1].tensors.items():
+        a = t[s0].clone()
+        t[s0].copy_(t[s1])
+        t[s1].copy_(a)
+    swapped = {}
+    for f in ("w_gate", "w_up", "w_down", "s_gate", "z_gate", "s_up", "z_up", "s_down", "z_down"):
+        arr = getattr(w, f).copy()
+        arr[[s0, s1]] = arr[[s1, s0]]
+        swapped[f] = arr
+    ref_sw = _oracle(case, **swapped)
+    assert np.abs(ref_sw["out"] - ref["out"]).max() > 0.1 * np.abs(ref["out"]).max()
+    torch.cuda.synchronize()
+    before = [o.cpu().view(torch.int16).numpy().copy() for o in outs]
+    with torch.cuda.stream(stream):
+        graph.replay()
+    stream.synchronize()
+    for i, o in enumerate(outs):
+        if i == 1:
+            assert_out_close(bf16_bits_to_f64(o), ref_sw["out"], what="rewritten pool copy")
+        else:
+            np.testing.assert_array_equal(o.cpu().view(torch.int16).numpy(), before[i], err_msg=f"layer {i}")
+            assert_out_close(bf16_bits_to_f64(o), ref["out"], what=f"layer {i} after the rewrite")
