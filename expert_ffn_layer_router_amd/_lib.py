@@ -86,6 +86,7 @@ def load():
                                        ctypes.POINTER(ctypes.c_int32)]),
         "moe_expert_bytes": (c_int, [vp, ctypes.POINTER(ctypes.c_uint64)]),
         "moe_forward": (c_int, [vp, i32, vp, vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp, sz, vp]),
+        "moe_forward_noalloc": (c_int, [vp, i32, vp, vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp]),
         "moe_routing_view": (c_int, [vp, vp, i32, ctypes.POINTER(MoeRouting)]),
         "moe_graph_capture": (c_int, [vp, i32, vp, vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp, sz, vp]),
         "moe_graph_launch": (c_int, [vp, vp]),

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -190,6 +191,9 @@ moe_status check_T(const moe_layer* h, int32_t T) {
   return MOE_OK;
 }
 
+// workspace_bytes value for checking every argument but the workspace
+constexpr size_t kNoWorkspace = ~size_t(0);
+
 moe_status check_forward_args(moe_handle h, int32_t T, const uint16_t* hidden, const float* router_w,
                               const float* router_bias, const int32_t* slot_table, const moe_weights* w,
                               uint16_t* out, void* workspace, size_t workspace_bytes, moe::Plan* plan) {
@@ -198,7 +202,7 @@ moe_status check_forward_args(moe_handle h, int32_t T, const uint16_t* hidden, c
   if ((st = check_T(h, T)) != MOE_OK) return st;
   moe::make_plan(h->ecfg, T, plan);
   if (T == 0) return MOE_OK;
-  if (!hidden || !router_w || !slot_table || !w || !out || !workspace)
+  if (!hidden || !router_w || !slot_table || !w || !out || (!workspace && workspace_bytes != kNoWorkspace))
     return fail(MOE_ERR_INVALID_ARG, "null pointer argument");
   if (!w->w_gate || !w->w_up || !w->w_down || !w->s_gate || !w->z_gate || !w->s_up || !w->z_up ||
       !w->s_down || !w->z_down)
@@ -212,6 +216,7 @@ moe_status check_forward_args(moe_handle h, int32_t T, const uint16_t* hidden, c
   const void* a2[] = {w->s_gate, w->z_gate, w->s_up, w->z_up, w->s_down, w->z_down};
   for (const void* p : a2)
     if (!aligned(p, 2)) return fail(MOE_ERR_INVALID_ARG, "pointer %p is not 2-byte aligned", p);
+  if (workspace_bytes == kNoWorkspace) return MOE_OK;  // the caller supplies the workspace later
   if (workspace_bytes < plan->total)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, T=%d needs %zu", workspace_bytes, T,
                 plan->total);
@@ -489,3 +494,83 @@ MOE_EXPORT const char* moe_status_string(moe_status s) {
 
 MOE_EXPORT const char* moe_last_error(void) { return g_last_error.c_str(); }
 
+// ---- Allocation-free forward -------------------------------------------------
+// moe_forward with the workspace taken from a fixed device array of this
+// library instead of the caller: for callers that cannot allocate device
+// memory.  Each device holds its own copy of the array until the process
+// ends; its address on a device comes from hipGetSymbolAddress, called once
+// per device with that device current, and only that address is handed to
+// the kernels.  Every call on a device shares the array.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+size_t g_scratch_clear[kMaxDevices] = {};  // leading bytes of the array cleared by a launched kernel
+
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The current device's copy of the scratch array; the first call on a device
+// looks its address up.
+moe_status scratch_of_current_device(void** ptr, int* device) {
+  hipError_t err = hipGetDevice(device);
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(err));
+  if (*device < 0 || *device >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "device %d outside [0, %d)", *device, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[*device]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(err));
+    g_scratch_ptr[*device] = p;
+  }
+  *ptr = g_scratch_ptr[*device];
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_EXPORT moe_status moe_forward_noalloc(moe_handle h, int32_t T, const uint16_t* hidden, const float* router_w,
+                                          const float* router_bias, const int32_t* slot_table,
+                                          const moe_weights* w, uint16_t* out, moe_stream stream) {
+  moe_status st = check_handle(h);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(h, T)) != MOE_OK) return st;
+  moe::Plan p;
+  moe::make_plan(h->ecfg, T, &p);
+  if (T == 0) return MOE_OK;
+  if (p.total > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                "T=%d needs %zu bytes of workspace; the static scratch holds %zu (use moe_forward with a "
+                "caller workspace)", T, p.total, kScratchBytes);
+  // every argument is checked before the first device call
+  if ((st = check_forward_args(h, T, hidden, router_w, router_bias, slot_table, w, out, nullptr, kNoWorkspace,
+                               &p)) != MOE_OK)
+    return st;
+  void* ws = nullptr;
+  int device = -1;
+  if ((st = scratch_of_current_device(&ws, &device)) != MOE_OK) return st;
+  if ((st = check_forward_args(h, T, hidden, router_w, router_bias, slot_table, w, out, ws, kScratchBytes, &p)) !=
+      MOE_OK)
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  {
+    // The control words at the start of the array must be zero before their
+    // first use (every call leaves them zero): clear them once per device, by
+    // a kernel on the caller's stream.
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_clear[device] < p.ctrl_bytes) {
+      clear_words_kernel<<<1, 256, 0, s>>>(static_cast<uint32_t*>(ws), (int)(p.ctrl_bytes / 4));
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return fail(MOE_ERR_HIP, "clearing the scratch control words: %s", hipGetErrorString(err));
+      g_scratch_clear[device] = p.ctrl_bytes;
+    }
+  }
+  return enqueue(h, p, hidden, router_w, router_bias, slot_table, w, out, ws, s, false);
+}

@@ -127,6 +127,16 @@ class MoeLayer:
                                                     workspace), self._stream(stream)))
         return out
 
+    def forward_noalloc(self, hidden, router_w, router_b, slot_table, weights: DeviceWeights, out, stream=None):
+        """moe_forward_noalloc: the forward with the library's own device scratch
+        instead of a workspace (calls on one device must not overlap).  `out`
+        [T, d] is the caller's."""
+        T = int(hidden.shape[0])
+        _lib.check(self.lib.moe_forward_noalloc(self.handle, T, _ptr(hidden), _ptr(router_w), _ptr(router_b),
+                                                _ptr(slot_table), ctypes.byref(weights.struct()), _ptr(out),
+                                                self._stream(stream)))
+        return out
+
     def capture(self, hidden, router_w, router_b, slot_table, weights: DeviceWeights, out, workspace,
                 stream):
         """Captures a forward into the handle's graph (buffers must outlive the graph)."""

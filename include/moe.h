@@ -152,6 +152,25 @@ moe_status moe_forward(moe_handle h, int32_t T, const uint16_t *hidden, const fl
                        const float *router_bias, const int32_t *slot_table, const moe_weights *w,
                        uint16_t *out, void *workspace, size_t workspace_bytes, moe_stream stream);
 
+/* moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The intermediates live in a fixed 16 MiB device
+ * array of the library instead, one copy per device, held until the process
+ * ends; the library allocates nothing, and the first call on a device only
+ * looks up that array's address and clears its control words with a kernel
+ * on `stream`.  Every call on one device shares the array, which keeps the
+ * last call's contents: calls that overlap in time on one device (other
+ * streams, other threads, other handles) race and must be serialised by the
+ * caller.  Arguments as for moe_forward; a shape whose moe_workspace_size(T)
+ * exceeds 16 MiB returns MOE_ERR_WORKSPACE_TOO_SMALL before anything is
+ * enqueued (all decode shapes up to T = 64 at d_model 4096 and d_ff 14336
+ * fit).  The routing and the device error flags of such a call stay in the
+ * library's array and are not readable through moe_routing_view or
+ * moe_device_flags; a bad slot still makes its expert contribute zero. */
+moe_status moe_forward_noalloc(moe_handle h, int32_t T, const uint16_t *hidden, const float *router_w,
+                               const float *router_bias, const int32_t *slot_table, const moe_weights *w,
+                               uint16_t *out, moe_stream stream);
+
 /* Fills `view` with device pointers to the routing a forward with T tokens
  * left in `workspace`.  Pointer arithmetic only. */
 moe_status moe_routing_view(moe_handle h, const void *workspace, int32_t T, moe_routing *view);
