@@ -50,9 +50,20 @@ CSRC = os.path.join(ROOT, "expert_ffn_layer_router_amd", "csrc")
 STREAM_MAX_TOKENS = 64   # the library's decode (weight-streaming) family runs up to this T
 
 
-def kernel_of_stage(stage, T):
+def dense_decode(shape) -> bool:
+    """Whether the library runs dense tiles for this shape (the rule of its
+    plan): at most 16 tokens, and an expert left without routed rows rare --
+    (1 - k/E)^T <= 0.02 over the routed experts -- and T E <= 1024.  The router
+    then runs in the gate/up launch."""
+    T, E, k = shape.T, shape.num_experts, shape.top_k
+    return 0 < T <= 16 and (1.0 - k / E) ** T <= 0.02 and T * E <= 1024
+
+
+def kernel_of_stage(stage, T, dense=False):
     """Name prefix of the kernel that runs a GEMM stage for T tokens."""
     if T <= STREAM_MAX_TOKENS:
+        if dense and stage == "gate_up":
+            return "stream_gemm_router_kernel"
         return {"gate_up": "stream_gemm_kernel<true", "down": "stream_gemm_kernel<false"}[stage]
     return {"gate_up": "prefill_gemm_kernel<true", "down": "prefill_gemm_kernel<false"}[stage]
 
@@ -74,9 +85,10 @@ def source_sha() -> str:
 # Sources that decide what a GEMM family's kernels read and write: the kernel
 # file, its headers, the plan (splits, tile sizes) and the row tiles it is given.
 GEMM_FAMILY_SOURCES = {
-    family: [os.path.join(CSRC, f) for f in (f"{family}.hip", "device_common.h", "plan.h", "regroup.h", "moe_api.hip")]
+    family: [os.path.join(CSRC, f) for f in (f"{family}.hip", "device_common.h", "plan.h", "regroup.h", "moe_api.hip")
+             + extra]
     + [os.path.join(ROOT, "include", "moe.h")]
-    for family in ("stream_gemm", "prefill_gemm")
+    for family, extra in (("stream_gemm", ("router_small.h",)), ("prefill_gemm", ()))
 }
 
 
@@ -106,6 +118,8 @@ def algorithmic_work(shape, counts):
     gate_up_bytes = gate_up_w + 2 * T * d + 2 * R * f   # + x rows read, h written (bf16)
     down_bytes = down_w + 2 * R * f + 2 * R * d         # + h read, y written (bf16-equivalent)
     layer_bytes = gate_up_w + down_w + 2 * T * d + 2 * T * d + 4 * E * d + 4 * E + 4 * (E + ns)
+    if dense_decode(shape):  # the router's inputs are read by the same launch
+        gate_up_bytes += 4 * E * d + 4 * E + 4 * (E + ns)
     return dict(active=active, R=R,
                 gate_up=dict(bytes=gate_up_bytes, flops=4 * R * d * f),
                 down=dict(bytes=down_bytes, flops=2 * R * d * f),
@@ -211,7 +225,7 @@ def summarize_pmc(dirs, out_path, copy_dirs=(), copy_bytes=1 << 30, workload="")
 def load_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from committed counter summaries, if they
     were taken on the current sources of its GEMM family; else None."""
-    family = kernel.split("_kernel")[0]
+    family = "stream_gemm" if kernel.startswith("stream_gemm") else "prefill_gemm"
     sha = family_sha(family)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_pmc.json"))):
         with open(path) as fh:
@@ -360,6 +374,7 @@ def run_workload(name, steps, warmup, torch, *, mode="layers", model_layers=32, 
     counts = probe.routing(ws, T)["counts"].cpu().numpy()
     work = algorithmic_work(shape, counts)
     plan_fused = T <= STREAM_MAX_TOKENS
+    dense = dense_decode(shape)
 
     nlay = graph_length(steps, model_layers) if mode == "layers" else 1
     pool_bytes = w.nbytes()
@@ -440,8 +455,11 @@ def run_workload(name, steps, warmup, torch, *, mode="layers", model_layers=32, 
                 stage_sum[key] = stage_sum.get(key, 0.0) + v
             L.set_stage_timing(0)
         # few tokens: the regroup runs inside the router kernel and the combine
-        # inside the down kernel -- no kernel of their own to time
+        # inside the down kernel -- no kernel of their own to time; dense tiles:
+        # the router runs inside the gate/up launch
         fused = ("regroup", "combine") if plan_fused else ()
+        if dense:
+            fused += ("router",)
         stage_us = {key: 1e3 * v / max(1, n_fw) for key, v in stage_sum.items() if key not in fused}
         log(f"{log_prefix}stage us: " + ", ".join(f"{key} {v:.1f}" for key, v in stage_us.items()))
 
@@ -472,8 +490,8 @@ def run_workload(name, steps, warmup, torch, *, mode="layers", model_layers=32, 
             achieved = work[dom]["flops"] / dur_s / 1e12
             roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": achieved / BF16_PEAK_TFLOPS}
-        roof["traffic"] = load_traffic(name, kernel_of_stage(dom, T))
-        roof.update({"kernel": kernel_of_stage(dom, T), "kernel_us": stage_us[dom],
+        roof["traffic"] = load_traffic(name, kernel_of_stage(dom, T, dense))
+        roof.update({"kernel": kernel_of_stage(dom, T, dense), "kernel_us": stage_us[dom],
                      "algorithmic_bytes": work[dom]["bytes"], "algorithmic_flops": work[dom]["flops"]})
         rec["roofline"] = roof
     ctx = dict(case=case, shape=shape, layers=layers, pools=pools, stream=stream, eager=eager, graph=graph,

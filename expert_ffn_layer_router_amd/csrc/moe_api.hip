@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -15,18 +16,18 @@
 
 namespace moe {
 
-void launch_gateup(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w, char* ws,
-                   hipStream_t s) {
+void launch_gateup(const moe_config& c, const Plan& p, const uint16_t* hidden, const int32_t* slot_table,
+                   const moe_weights& w, char* ws, hipStream_t s) {
   if (p.family == GemmFamily::kStream)
-    launch_gateup_stream(c, p, hidden, w, ws, s);
+    launch_gateup_stream(c, p, hidden, slot_table, w, ws, s);
   else
     launch_gateup_prefill(c, p, hidden, w, ws, s);
 }
 
-void launch_down(const moe_config& c, const Plan& p, const moe_weights& w, uint16_t* out, char* ws,
-                 hipStream_t s) {
+void launch_down(const moe_config& c, const Plan& p, const int32_t* slot_table, const moe_weights& w, uint16_t* out,
+                 char* ws, hipStream_t s) {
   if (p.family == GemmFamily::kStream)
-    launch_down_stream(c, p, w, out, ws, s);
+    launch_down_stream(c, p, slot_table, w, out, ws, s);
   else
     launch_down_prefill(c, p, w, ws, s);
 }
@@ -101,6 +102,10 @@ bool api_check_handle(moe_handle h, const moe_config** cfg) {
 }
 }  // namespace moe
 
+#ifndef MOE_DENSE_IDLE_MAX
+#define MOE_DENSE_IDLE_MAX 0.02  // dense tiles while an expert without routed rows is at most this likely
+#endif
+
 namespace moe {
 
 void make_plan(const moe_config& c, int T, Plan* p) {
@@ -134,6 +139,18 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   }
   // GEMM row tiles: sum_e ceil(c_e / rows) <= ceil(R / rows) + (non-empty experts)
   p->max_tiles = (p->R + p->tile_rows - 1) / p->tile_rows + std::min(E, p->R);
+  // Dense tiles: with at most 16 tokens an expert's rows fit one 16-row tile,
+  // whose matrix-core work is the same whichever tokens fill it, so every
+  // expert can take all T tokens: the gate/up GEMM then needs no routing and
+  // runs beside the router; the down GEMM, after it, takes the routed rows.  Worth
+  // it when an expert without routed rows -- whose gate/up weights are then
+  // streamed for nothing -- is rare: each token picks k of Er experts, so an
+  // expert gets no row with probability about (1 - k/Er)^T under even routing.
+  {
+    const int kr = c.top_k - c.num_shared;
+    const double idle = std::pow(1.0 - (double)kr / Er, (double)T);
+    p->dense = T <= kStreamTileRows && T <= kStreamMaxTokens && idle <= MOE_DENSE_IDLE_MAX && T * Er <= 1024;
+  }
   // split the down projection's k range until the grid has enough blocks
   if (p->family == GemmFamily::kStream) {
     p->gateup_ncw = (kStreamMaxNCW >= 2 && c.d_ff % 128 == 0) ? 2 : 1;
@@ -152,8 +169,10 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   };
   const size_t R = (size_t)p->R;
   // control words, laid out the same for every T: [0] router ticket,
-  // [1 + i] combine ticket of output column slice i
-  p->ctrl = take(4 * (1 + (size_t)c.d_model / kStreamCols));
+  // [1 + i] combine ticket of output column slice i, then per expert the
+  // token mask the router publishes for dense gate/up tiles
+  p->tmask = 4 * (1 + (size_t)c.d_model / kStreamCols);
+  p->ctrl = take(p->tmask + 4 * (size_t)E);
   p->ctrl_bytes = off;  // aligned end of the control words (they start at offset 0)
   p->flags = take(4);
   p->logits = take(sizeof(double) * (size_t)std::max({1, p->router_split, p->small_split}) * T * Er);
@@ -167,7 +186,8 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   p->xsum = take(4 * (size_t)T);
   p->hsum_part = take(4 * R * (size_t)(c.d_ff / 128));
   p->num_tiles = take(4);
-  p->h = take(2 * R * (size_t)c.d_ff);
+  // dense tiles: h holds every expert's rows for all T tokens
+  p->h = take(2 * (p->dense ? (size_t)E * T : R) * (size_t)c.d_ff);
   p->y = take(4 * (size_t)p->down_split * R * (size_t)c.d_model);
   // prefill: x in the GEMMs' fragment k-order
   p->xperm = take(p->family == GemmFamily::kPrefill ? 2 * (size_t)T * c.d_model : 0);
@@ -235,15 +255,20 @@ moe_status enqueue(moe_layer* h, const moe::Plan& p, const uint16_t* hidden, con
   };
   // with few tokens the regroup runs inside the router kernel and the
   // combine inside the down kernel (their stages then time as empty)
+  // with dense tiles the router runs in the gate/up launch (its stages then
+  // time as empty too)
   const moe_config& c = h->ecfg;
   mark(0);
-  moe::launch_router(c, p, hidden, router_w, router_bias, slot_table, ws, s);
+  if (!p.dense) moe::launch_router(c, p, hidden, router_w, router_bias, slot_table, ws, s);
   mark(1);
   if (!p.fused_small) moe::launch_permute(c, p, slot_table, ws, s);
   mark(2);
-  moe::launch_gateup(c, p, hidden, *w, ws, s);
+  if (p.dense)
+    moe::launch_gateup_router_stream(c, p, hidden, router_w, router_bias, slot_table, *w, ws, s);
+  else
+    moe::launch_gateup(c, p, hidden, slot_table, *w, ws, s);
   mark(3);
-  moe::launch_down(c, p, *w, out, ws, s);
+  moe::launch_down(c, p, slot_table, *w, out, ws, s);
   mark(4);
   if (!p.fused_small) moe::launch_combine(c, p, out, ws, s);
   mark(5);

@@ -55,9 +55,12 @@ struct Plan {
   int down_split = 1;         // k-split of the down projection
   int max_tiles = 0;          // upper bound on GEMM row tiles
   bool fused_small = false;   // few tokens: router + top-k + regroup in one kernel, combine fused into down
+  // few tokens and nearly every expert routed to: dense tiles (every expert
+  // with all T tokens), the router launched beside the gate/up GEMM
+  bool dense = false;
   // byte offsets into the workspace; [ctrl, ctrl + ctrl_bytes) are control
   // words that must be zero before first use and are left zero by every call
-  size_t ctrl = 0, ctrl_bytes = 0, flags = 0, logits = 0, topk_idx = 0, topk_w = 0, counts = 0,
+  size_t ctrl = 0, ctrl_bytes = 0, tmask = 0, flags = 0, logits = 0, topk_idx = 0, topk_w = 0, counts = 0,
          offsets = 0, perm = 0, inv = 0, tiles = 0, num_tiles = 0, xsum = 0, hsum_part = 0, h = 0, y = 0,
          xperm = 0, rhist = 0, total = 0;
 };
@@ -67,20 +70,27 @@ void make_plan(const moe_config& c, int T, Plan* p);
 
 struct RegroupArgs;
 RegroupArgs regroup_args(const moe_config& c, const Plan& p, const int32_t* slot_table, char* ws);
+struct RouterSmallArgs;
+RouterSmallArgs router_small_args(const moe_config& c, const Plan& p, const uint16_t* hidden, const float* router_w,
+                                  const float* router_bias, const int32_t* slot_table, char* ws);
 
 // Kernel launchers (enqueue only).
 void launch_router(const moe_config& c, const Plan& p, const uint16_t* hidden, const float* router_w,
                    const float* router_bias, const int32_t* slot_table, char* ws, hipStream_t s);
 void launch_permute(const moe_config& c, const Plan& p, const int32_t* slot_table, char* ws, hipStream_t s);
-void launch_gateup(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w, char* ws,
-                   hipStream_t s);
-void launch_down(const moe_config& c, const Plan& p, const moe_weights& w, uint16_t* out, char* ws,
-                 hipStream_t s);
+void launch_gateup(const moe_config& c, const Plan& p, const uint16_t* hidden, const int32_t* slot_table,
+                   const moe_weights& w, char* ws, hipStream_t s);
+void launch_down(const moe_config& c, const Plan& p, const int32_t* slot_table, const moe_weights& w, uint16_t* out,
+                 char* ws, hipStream_t s);
 // decode family (stream_gemm.hip); with p.fused_small the down launch also writes out
-void launch_gateup_stream(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w,
-                          char* ws, hipStream_t s);
-void launch_down_stream(const moe_config& c, const Plan& p, const moe_weights& w, uint16_t* out, char* ws,
-                        hipStream_t s);
+void launch_gateup_stream(const moe_config& c, const Plan& p, const uint16_t* hidden, const int32_t* slot_table,
+                          const moe_weights& w, char* ws, hipStream_t s);
+// p.dense: the router and the gate/up GEMM in one launch
+void launch_gateup_router_stream(const moe_config& c, const Plan& p, const uint16_t* hidden, const float* router_w,
+                                 const float* router_bias, const int32_t* slot_table, const moe_weights& w,
+                                 char* ws, hipStream_t s);
+void launch_down_stream(const moe_config& c, const Plan& p, const int32_t* slot_table, const moe_weights& w,
+                        uint16_t* out, char* ws, hipStream_t s);
 // prefill family (prefill_gemm.hip)
 void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w,
                            char* ws, hipStream_t s);

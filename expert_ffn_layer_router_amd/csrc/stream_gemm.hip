@@ -35,6 +35,7 @@
 // expert rows, in the same fixed order as the stand-alone combine kernel.
 #include "device_common.h"
 #include "plan.h"
+#include "router_small.h"
 
 namespace moe {
 
@@ -60,6 +61,11 @@ __device__ __forceinline__ void load_lds16(const void* g, char* lds_base) {
 // 4 bytes: lane l of the wave writes lds_base + 4 l.
 __device__ __forceinline__ void load_lds4(const void* g, char* lds_base) {
   __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds_base, 4, 0, 0);
+}
+// The same with the sc1 cache bit: coherent with stores of other blocks made
+// with device-scope atomics (it reads past this XCD's L2).
+__device__ __forceinline__ void load_lds4_coherent(const void* g, char* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds_base, 4, 0, 16 /* sc1 */);
 }
 
 // Wait until at most `n` vector-memory operations of this wave are pending.
@@ -103,6 +109,12 @@ __device__ __forceinline__ uint32_t lds_read_u16(const char* p) {
   asm volatile("ds_read_u16 %0, %1" : "=v"(v) : "v"(addr));
   return v;
 }
+__device__ __forceinline__ uint32_t lds_read_b32(const char* p) {
+  uint32_t v;
+  const uint32_t addr = (uint32_t)(uintptr_t)(const lds_void*)p;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void lds_ready(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
@@ -125,6 +137,7 @@ struct StreamArgs {
   const int4* tiles;
   const int32_t* num_tiles;
   int num_slots, d, dff, topk, R, kchunk;
+  int max_tiles;             // grid rows of tiles (dense tiles: every expert)
   const uint8_t* w0;         // gate (or down) codes
   const uint8_t* w1;         // up codes (gate/up only)
   const uint16_t *s0, *z0, *s1, *z1;
@@ -132,16 +145,24 @@ struct StreamArgs {
   float* ypart;              // down output [split][R][d]
   uint32_t* flags;
   FusedCombine fc;
+  // Dense tiles (few tokens, experts that are nearly all routed to): gate/up
+  // tile e is expert e with all T tokens in token order, h rows e*T .. e*T+T-1,
+  // so it needs no routing (and raises no bad-slot flag: only experts with
+  // routed rows may, in the down GEMM); the down GEMM runs the routed tiles
+  // and reads the row of grouped position p at e*T + (token of p).
+  int dense, T;
+  const int32_t* slot_table;  // [E] dense gate/up tiles: the slot of expert e
+  int num_experts;            // E (routed and shared)
+  uint32_t* tmask;            // [E] dense plans: the router's token masks (control words)
 };
 
 // Fused combine: the last block to finish a column slice (an atomic ticket
 // per slice) gathers that slice of out[] for every token: per token the k
 // routed rows in order j = 0..k-1, each the fixed-order sum of its k-splits.
 template <int COLS>
-__device__ void fused_combine_tail(const StreamArgs& a, int bx, int ntiles) {
+__device__ void fused_combine_tail(const StreamArgs& a, int bx, int ntiles, int nsplit) {
   __shared__ int is_last;
-  if (!last_block_ticket(&a.fc.tickets[bx], (uint32_t)(ntiles * gridDim.z), &is_last)) return;
-  const int nsplit = gridDim.z;
+  if (!last_block_ticket(&a.fc.tickets[bx], (uint32_t)(ntiles * nsplit), &is_last)) return;
   const int n0 = bx * COLS;
   __shared__ int rp[kStreamMaxTokens * 8];
   __shared__ float rw[kStreamMaxTokens * 8];
@@ -185,10 +206,18 @@ __device__ void fused_combine_tail(const StreamArgs& a, int bx, int ntiles) {
 // running sums; the (s, z) of a stage's groups are copied into LDS beside
 // its weights (one more 1 KB copy per stage).  Per-row formats apply (s, z)
 // once, in the epilogue.
-template <bool GATEUP, int NCW, int NBUF, int KW, bool NT, int RG, int BITS, bool GROUPED>
-__global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(GROUPED ? (RG == 1 ? 3 : 2) : (RG == 1 ? MOE_STREAM_WPE : 3))))
-void stream_gemm_kernel(StreamArgs a) {
+// The stage ring, and for dense gate/up tiles two words per wave after it
+// that receive the router's token mask.
+template <bool GATEUP, int NCW, int NBUF, int BITS, bool GROUPED, bool DENSE = false>
+constexpr int stream_smem_bytes() {
+  return NBUF * ((GATEUP ? 2 : 1) * 64 * NCW * kWRowBytes + (GROUPED ? kPBytes : 0)) + (DENSE ? 4 * 8 : 0);
+}
+
+// One block: column slice bx, row tile by, k-split bz of nz; smem holds
+// stream_smem_bytes<...>() bytes, 1 KB aligned.  DENSE: a gate/up block of
+// dense tiles (tile by is expert by with all T tokens).
+template <bool GATEUP, int NCW, int NBUF, int KW, bool NT, int RG, int BITS, bool GROUPED, bool DENSE = false>
+__device__ __forceinline__ void stream_gemm_body(const StreamArgs& a, int bx, int by, int bz, int nz, char* smem) {
   static_assert(NBUF == 2 || NBUF == 3, "stage ring of 2 or 3 buffers");
   static_assert(KW == 2 || KW == 4, "k split over 2 or 4 waves");
   static_assert(RG == 1 || RG == 2, "tiles of 16 or 32 rows");
@@ -213,17 +242,24 @@ void stream_gemm_kernel(StreamArgs a) {
   static_assert(!GROUPED || (kQGroup % KR == 0 && SK <= 2 * kQGroup), "a wave's k part lies in one group");
   static_assert(!GROUPED || 4 * 2 * COLS * 2 == kPBytes, "4 arrays x 2 groups x 64 columns of fp16 per stage");
   static_assert(WI * kRowsPerWInst * 4 == NWR, "even split over waves");
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * SBYTES];
+  static_assert(NBUF * SBYTES == stream_smem_bytes<GATEUP, NCW, NBUF, BITS, GROUPED>(), "stage ring size");
+  char* const mask_slots = smem + NBUF * SBYTES + 8 * (threadIdx.x >> 6);  // dense tiles: this wave's polls
 
-  const int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;  // column slice, row tile, k-split
-  const int ntiles = *a.num_tiles;
+  constexpr bool dense_tile = GATEUP && DENSE;
+  static_assert(!dense_tile || RG == 1, "dense tiles hold at most 16 tokens");
+  const int ntiles = dense_tile ? a.max_tiles : *a.num_tiles;
   const int tile = by;
   if (tile >= ntiles) return;
+  // dense plans: the down GEMM's first block returns the router's token
+  // masks to zero for the next call (every gate/up block has finished)
+  if (!GATEUP && a.dense && bx == 0 && tile == 0 && bz == 0)
+    for (int x = threadIdx.x; x < a.num_experts; x += 256) reset_ticket(&a.tmask[x]);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, grp = lane >> 4;
   const int kp = wave % KW, cp = wave / KW;
   const int n0 = bx * COLS;
-  const int4 td = a.tiles[tile];  // (expert, slot, first grouped row, rows <= 16 RG)
+  // (expert, slot, first grouped row, rows <= 16 RG); dense gate/up: expert `tile`, all tokens
+  const int4 td = dense_tile ? make_int4(tile, a.slot_table[tile], tile * a.T, a.T) : a.tiles[tile];
   const int slot = td.y, pbase = td.z, rows = td.w;
   const int ncols_total = GATEUP ? a.dff : a.d;
   const int K = GATEUP ? a.d : a.kchunk;
@@ -233,7 +269,7 @@ void stream_gemm_kernel(StreamArgs a) {
   float* yrow = GATEUP ? nullptr : a.ypart + ((size_t)bz * a.R + pbase) * a.d;
 
   if (bad) {
-    if (threadIdx.x == 0) atomicOr(a.flags, MOE_FLAG_BAD_SLOT);
+    if (threadIdx.x == 0 && !dense_tile) atomicOr(a.flags, MOE_FLAG_BAD_SLOT);
     if (GATEUP) return;
     for (int i = threadIdx.x; i < rows * COLS; i += 256) store_coherent(&yrow[(size_t)(i / COLS) * a.d + n0 + i % COLS], 0.0f);
   } else {
@@ -244,8 +280,9 @@ void stream_gemm_kernel(StreamArgs a) {
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
       const int mm = lr + 16 * g < rows ? lr + 16 * g : 0;
-      asrc[g] = GATEUP ? a.act + (size_t)(a.perm[pbase + mm] / a.topk) * a.d + ka
-                       : a.act + (size_t)(pbase + mm) * a.dff + kbeg + ka;
+      const int tok = dense_tile ? mm : a.perm[pbase + mm] / a.topk;  // the token of tile row mm
+      const int hrow = a.dense ? td.x * a.T + tok : pbase + mm;       // down: its row of h
+      asrc[g] = GATEUP ? a.act + (size_t)tok * a.d + ka : a.act + (size_t)hrow * a.dff + kbeg + ka;
     }
     const uint8_t* wsrc[WI];
 #pragma unroll
@@ -410,22 +447,80 @@ void stream_gemm_kernel(StreamArgs a) {
     // waiting until that many are pending completes W(s).  The last NBUF - 1
     // stages issue no weight copies and wait for all.
     constexpr int kPending = (NBUF - 1) * (WI + (GROUPED ? 1 : 0)) + RG * KS;
-    u32x4 anx[RG][KS], acur[RG][KS];
-    load_a(0, anx);
+    // The activation fragments of stage st + 1 are loaded one stage ahead.
+    // Dense tiles use two register sets in turn (a loop unrolled twice): there,
+    // copying a prefetched set into a working one at the top of each stage
+    // made the compiler wait for every load in flight, the poll and the next
+    // stage's weight copies included.
+    u32x4 aset0[RG][KS], aset1[RG][KS];
+    load_a(0, aset0);
     issue_w(0);
     if (NBUF == 3 && nst > 1) issue_w(1);
-    const int nmain = max(0, nst - (NBUF - 1));
-    for (int st = 0; st < nmain; ++st) {
-#pragma unroll
-      for (int g = 0; g < RG; ++g)
-#pragma unroll
-        for (int j = 0; j < KS; ++j) acur[g][j] = anx[g][j];
-      load_a(st + 1, anx);
+    // Dense tiles: until the router publishes the expert's token mask, tile
+    // row r is token r for every r; once a wave sees the mask it loads only
+    // the routed tokens' rows (the other lanes repeat the first routed row, so
+    // their loads coalesce), which cuts the activation traffic.  Row r stays
+    // token r, so a routed token's products are whole whenever the switch
+    // happens; the other rows' h is never read.  Stage st's poll is a coherent
+    // direct-to-LDS load by lane 0 into this wave's slot st % 2, issued after
+    // the stage's copies; the copy wait of stage st lets it stay in flight and
+    // that of stage st + 1 completes it, so no register ever waits on it.  The
+    // poll before the loop (slot 1) gives the first stage a value.  Every
+    // stage polls, so that every stage leaves the same number of loads in
+    // flight (a branch around the poll made the compiler wait for all of them).
+    uint32_t known = 0;
+    auto poll = [&](int st) {
+      if constexpr (dense_tile)
+        if (lane == 0) load_lds4_coherent(a.tmask + td.x, mask_slots + 4 * (st & 1));
+    };
+    poll(-1);
+    // stage st of the main loop: its fragments are in `use`, stage st + 1's go to `fill`
+    auto main_stage = [&](int st, const u32x4 (&use)[RG][KS], u32x4 (&fill)[RG][KS]) {
+      load_a(st + 1, fill);
       issue_w(st + NBUF - 1);
-      wait_vmem<kPending>();
+      poll(st);
+      wait_vmem<kPending + (dense_tile ? 1 : 0)>();
+      if constexpr (dense_tile) {
+        uint32_t polled = lds_read_b32(mask_slots + 4 * ((st + 1) & 1));  // the previous poll
+        lds_wait();
+        lds_ready(polled);
+        if (!(known & kMaskKnown) && (polled & kMaskKnown)) {  // wave-uniform
+          known = polled;
+          const uint32_t m = known & 0xFFFFu;
+          const int row = ((m >> lr) & 1u) ? lr : (m ? __builtin_ctz(m) : 0);
+          asrc[0] = a.act + (size_t)row * a.d + KR * kp + (KR / 4) * grp;
+        }
+      }
       lds_barrier();
-      compute(st, acur);
+      compute(st, use);
       lds_barrier();
+    };
+    const int nmain = max(0, nst - (NBUF - 1));
+    if constexpr (dense_tile) {
+      int st = 0;
+      for (; st + 1 < nmain; st += 2) {
+        main_stage(st, aset0, aset1);
+        main_stage(st + 1, aset1, aset0);
+      }
+      if (st < nmain) {
+        main_stage(st, aset0, aset1);
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+          for (int j = 0; j < KS; ++j) aset0[g][j] = aset1[g][j];
+      }
+    } else {
+      // (one set copied into the other per stage: the compiler waits for the
+      // copied loads without holding back the weight copies here, and this
+      // form measured slightly faster than the unrolled one)
+      for (int st = 0; st < nmain; ++st) {
+        u32x4 acur[RG][KS];
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+          for (int j = 0; j < KS; ++j) acur[g][j] = aset0[g][j];
+        main_stage(st, acur, aset0);
+      }
     }
     // per-row formats: scale and code offset (bias + z) of this wave's
     // columns, loaded while the last stages land (grouped: already applied)
@@ -439,11 +534,13 @@ void stream_gemm_kernel(StreamArgs a) {
       cc[t] = GROUPED ? 0.0f : kBias + fp16_to_f32((up ? a.z1 : a.z0)[sbase + nl]);
     }
     for (int st = nmain; st < nst; ++st) {
+      // the last stages: no weight copies left to keep in flight
+      u32x4 acur[RG][KS];
 #pragma unroll
       for (int g = 0; g < RG; ++g)
 #pragma unroll
-        for (int j = 0; j < KS; ++j) acur[g][j] = anx[g][j];
-      if (st + 1 < nst) load_a(st + 1, anx);
+        for (int j = 0; j < KS; ++j) acur[g][j] = aset0[g][j];
+      if (st + 1 < nst) load_a(st + 1, aset0);
       wait_vmem<0>();
       lds_barrier();
       compute(st, acur);
@@ -495,7 +592,40 @@ void stream_gemm_kernel(StreamArgs a) {
   }
 
   if (GATEUP || a.fc.tickets == nullptr) return;
-  fused_combine_tail<COLS>(a, bx, ntiles);
+  fused_combine_tail<COLS>(a, bx, ntiles, nz);
+}
+
+template <bool GATEUP, int NCW, int NBUF, int KW, bool NT, int RG, int BITS, bool GROUPED>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(GROUPED ? (RG == 1 ? 3 : 2) : (RG == 1 ? MOE_STREAM_WPE : 3))))
+void stream_gemm_kernel(StreamArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[stream_smem_bytes<GATEUP, NCW, NBUF, BITS, GROUPED>()];
+  stream_gemm_body<GATEUP, NCW, NBUF, KW, NT, RG, BITS, GROUPED>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z,
+                                                                  smem);
+}
+
+// The router beside the gate/up GEMM of dense tiles (few tokens, nearly every
+// expert routed to): with dense tiles the gate/up GEMM does not depend on the
+// routing, so both run in one launch and the router's latency hides behind
+// the weight stream.  Blocks 0 .. nrouter-1 are the router's (expert
+// b % E, k-split b / E, all T <= 16 tokens); the rest are gate/up blocks in the
+// order of the stand-alone kernel's grid (column slice fastest).  Neither
+// waits for the other; the down GEMM, the next launch, reads the routing.
+constexpr int kDenseRouterLogits = 1024;  // T x E logits the router's finish stages in LDS
+template <int NCW, int NBUF, int KW, bool NT, int BITS, bool GROUPED>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(GROUPED ? 3 : (NCW == 2 ? 2 : MOE_STREAM_WPE))))
+void stream_gemm_router_kernel(StreamArgs a, RouterSmallArgs r, int nrouter) {
+  constexpr int kGemm = stream_smem_bytes<true, NCW, NBUF, BITS, GROUPED, true>();
+  constexpr int kRouter = router_small_lds_bytes<kDenseRouterLogits, kRouterTokTile>();
+  __shared__ __attribute__((aligned(1024))) char smem[kGemm > kRouter ? kGemm : kRouter];
+  const int b = blockIdx.x;
+  if (b < nrouter) {
+    router_small_body<kDenseRouterLogits, kRouterTokTile, 8>(r, b % r.E, 0, b / r.E, nrouter, smem);
+    return;
+  }
+  const int g = b - nrouter, ncb = a.dff / (64 * NCW);
+  stream_gemm_body<true, NCW, NBUF, KW, NT, 1, BITS, GROUPED, true>(a, g % ncb, g / ncb, 0, 1, smem);
 }
 
 namespace {
@@ -507,6 +637,9 @@ namespace {
 #endif
 #ifndef MOE_STREAM_KW_DN
 #define MOE_STREAM_KW_DN 4
+#endif
+#ifndef MOE_DENSE_NCW
+#define MOE_DENSE_NCW 1
 #endif
 // Weights are streamed with the nt hint: most lines are read once per launch,
 // and early eviction keeps the activations and the router's inputs (read
@@ -545,18 +678,31 @@ void launch_stream_format(const moe_config& c, const Plan& p, const StreamArgs& 
 }
 }  // namespace
 
-void launch_gateup_stream(const moe_config& c, const Plan& p, const uint16_t* hidden, const moe_weights& w,
-                          char* ws, hipStream_t s) {
+// Fields of the arguments both GEMMs share.
+void stream_common_args(const moe_config& c, const Plan& p, const int32_t* slot_table, char* ws, StreamArgs* a) {
+  a->tiles = reinterpret_cast<const int4*>(ws + p.tiles);
+  a->num_tiles = reinterpret_cast<const int32_t*>(ws + p.num_tiles);
+  a->num_slots = c.num_slots;
+  a->d = c.d_model;
+  a->dff = c.d_ff;
+  a->topk = c.top_k;
+  a->R = p.R;  // rows of the down output
+  a->max_tiles = p.max_tiles;
+  a->flags = reinterpret_cast<uint32_t*>(ws + p.flags);
+  a->dense = p.dense ? 1 : 0;
+  a->T = p.T;
+  a->slot_table = slot_table;
+  a->perm = reinterpret_cast<const int32_t*>(ws + p.perm);
+  a->num_experts = c.num_experts;
+  a->tmask = reinterpret_cast<uint32_t*>(ws + p.ctrl + p.tmask);
+}
+
+StreamArgs gateup_stream_args(const moe_config& c, const Plan& p, const uint16_t* hidden, const int32_t* slot_table,
+                              const moe_weights& w, char* ws) {
   StreamArgs a{};
+  stream_common_args(c, p, slot_table, ws, &a);
   a.act = hidden;
   a.perm = reinterpret_cast<const int32_t*>(ws + p.perm);
-  a.tiles = reinterpret_cast<const int4*>(ws + p.tiles);
-  a.num_tiles = reinterpret_cast<const int32_t*>(ws + p.num_tiles);
-  a.num_slots = c.num_slots;
-  a.d = c.d_model;
-  a.dff = c.d_ff;
-  a.topk = c.top_k;
-  a.R = p.R;
   a.w0 = w.w_gate;
   a.w1 = w.w_up;
   a.s0 = w.s_gate;
@@ -564,27 +710,48 @@ void launch_gateup_stream(const moe_config& c, const Plan& p, const uint16_t* hi
   a.s1 = w.s_up;
   a.z1 = w.z_up;
   a.h = reinterpret_cast<uint16_t*>(ws + p.h);
-  a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
-  launch_stream_format<true>(c, p, a, p.gateup_ncw, s);
+  return a;
 }
 
-void launch_down_stream(const moe_config& c, const Plan& p, const moe_weights& w, uint16_t* out, char* ws,
-                        hipStream_t s) {
+void launch_gateup_stream(const moe_config& c, const Plan& p, const uint16_t* hidden, const int32_t* slot_table,
+                          const moe_weights& w, char* ws, hipStream_t s) {
+  launch_stream_format<true>(c, p, gateup_stream_args(c, p, hidden, slot_table, w, ws), p.gateup_ncw, s);
+}
+
+void launch_gateup_router_stream(const moe_config& c, const Plan& p, const uint16_t* hidden, const float* router_w,
+                                 const float* router_bias, const int32_t* slot_table, const moe_weights& w,
+                                 char* ws, hipStream_t s) {
+  StreamArgs a = gateup_stream_args(c, p, hidden, slot_table, w, ws);
+  a.max_tiles = c.num_experts;  // one dense tile per expert
+  const RouterSmallArgs r = router_small_args(c, p, hidden, router_w, router_bias, slot_table, ws);
+  const int nrouter = r.E * p.small_split;  // T <= 16: one token group
+  constexpr int KW = MOE_STREAM_KW_GU;
+  constexpr int NCW = MOE_DENSE_NCW;  // per-row formats: blocks of 64 NCW columns
+  if (c.weight_bits == 8) {
+    const dim3 grid(nrouter + c.num_experts * (c.d_ff / (64 * (c.group_size ? 1 : NCW))));
+    if (c.group_size)
+      stream_gemm_router_kernel<1, MOE_STREAM_NBUF, KW, true, 8, true><<<grid, 256, 0, s>>>(a, r, nrouter);
+    else
+      stream_gemm_router_kernel<NCW, MOE_STREAM_NBUF, KW, true, 8, false><<<grid, 256, 0, s>>>(a, r, nrouter);
+  } else {
+    const dim3 grid(nrouter + c.num_experts * (c.d_ff / (64 * (c.group_size ? 1 : NCW))));
+    if (c.group_size)
+      stream_gemm_router_kernel<1, MOE_STREAM_NBUF, KW, true, 4, true><<<grid, 256, 0, s>>>(a, r, nrouter);
+    else
+      stream_gemm_router_kernel<NCW, MOE_STREAM_NBUF, KW, true, 4, false><<<grid, 256, 0, s>>>(a, r, nrouter);
+  }
+}
+
+void launch_down_stream(const moe_config& c, const Plan& p, const int32_t* slot_table, const moe_weights& w,
+                        uint16_t* out, char* ws, hipStream_t s) {
   StreamArgs a{};
+  stream_common_args(c, p, slot_table, ws, &a);
   a.act = reinterpret_cast<const uint16_t*>(ws + p.h);
-  a.tiles = reinterpret_cast<const int4*>(ws + p.tiles);
-  a.num_tiles = reinterpret_cast<const int32_t*>(ws + p.num_tiles);
-  a.num_slots = c.num_slots;
-  a.d = c.d_model;
-  a.dff = c.d_ff;
-  a.topk = c.top_k;
-  a.R = p.R;
   a.kchunk = c.d_ff / p.down_split;
   a.w0 = w.w_down;
   a.s0 = w.s_down;
   a.z0 = w.z_down;
   a.ypart = reinterpret_cast<float*>(ws + p.y);
-  a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
   if (p.fused_small) {
     a.fc.tickets = reinterpret_cast<uint32_t*>(ws + p.ctrl) + 1;
     a.fc.inv = reinterpret_cast<const int32_t*>(ws + p.inv);

@@ -68,17 +68,18 @@ def test_create_accepts_shared_expert_limits(lib, kw):
 
 def test_shared_experts_add_rows_to_the_workspace(lib):
     """With S shared experts every token has k + S rows: the workspace grows like
-    a layer with top_k + S, beyond the routed-only one."""
+    a layer with top_k + S, beyond the routed-only one.  (Token counts past 16:
+    at most 16 tokens can run dense tiles, whose rows follow the experts.)"""
     sizes = {}
     for k, S in ((2, 0), (2, 2), (4, 0)):
         st, h = _create(lib, top_k=k, num_shared=S, num_experts=8, max_tokens=4096)
         assert st == 0
         n = ctypes.c_size_t()
-        for T in (16, 4096):
+        for T in (40, 4096):
             assert lib.moe_workspace_size(h, T, ctypes.byref(n)) == 0
             sizes[(k, S, T)] = n.value
         lib.moe_destroy(h)
-    for T in (16, 4096):
+    for T in (40, 4096):
         assert sizes[(2, 0, T)] < sizes[(2, 2, T)]
         # same rows as top-4, at most the few bytes of two more groups' counters apart
         assert abs(sizes[(2, 2, T)] - sizes[(4, 0, T)]) <= 2048

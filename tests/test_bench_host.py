@@ -10,11 +10,17 @@ import synth
 def test_algorithmic_bytes_of_the_decode_gate_up_launch():
     """8 active Mixtral-shaped int4 experts: gate and up codes (d d_ff / 2 bytes
     each) and fp16 (s, z) per output row of both, plus the 16 x rows read and
-    the 32 h rows written in bf16 -- worked out by hand."""
+    the 32 h rows written in bf16 -- worked out by hand; the router runs in the
+    same launch (dense tiles), so its fp32 weights, bias and the slot table
+    count too."""
     shape = synth.case_shape("mixtral_decode")
     work = bench.algorithmic_work(shape, [4] * 8)
     per_expert = 2 * 14336 * 4096 // 2 + 2 * 2 * 2 * 14336
-    assert work["gate_up"]["bytes"] == 8 * per_expert + 2 * 16 * 4096 + 2 * 32 * 14336 == 471728128
+    router = 4 * 8 * 4096 + 4 * 8 + 4 * 8
+    assert work["gate_up"]["bytes"] == 8 * per_expert + 2 * 16 * 4096 + 2 * 32 * 14336 + router == 471859264
+    fine = synth.case_shape("fine_decode")      # routed tiles: the router has a launch of its own
+    per_fine = 2 * 2048 * 4096 // 2 + 2 * 2 * 2 * 2048
+    assert bench.algorithmic_work(fine, [1] * 64)["gate_up"]["bytes"] == 64 * per_fine + 2 * 16 * 4096 + 2 * 96 * 2048
     assert work["gate_up"]["flops"] == 4 * 32 * 4096 * 14336
     assert work["down"]["flops"] == 2 * 32 * 4096 * 14336
 
@@ -74,3 +80,26 @@ def test_graph_length_divides_the_step_count():
     assert bench.graph_length(256) == 32
     assert bench.graph_length(5) == 5
     assert bench.graph_length(7) == 7
+
+
+def test_dense_rule_matches_the_library_plan():
+    """bench.py's copy of the library's dense-tile rule: a dense plan keeps h
+    rows for every expert and token (2 E T d_ff bytes and more), the routed plan
+    only for the T k routed rows, which is less."""
+    import ctypes
+    from expert_ffn_layer_router_amd import _lib
+    lib = _lib.load()
+    for name, T in [("mixtral_decode", 16), ("mixtral_decode", 12), ("mixtral_decode", 3), ("mixtral_decode", 1),
+                    ("fine_decode", 16), ("phi35_skew", 64), ("phi35_skew", 16), ("shared_decode", 16)]:
+        s = synth.case_shape(name, T=T)
+        cfg = _lib.MoeConfig(s.d_model, s.d_ff, s.num_experts, s.top_k, s.num_slots, 64, 0, s.num_shared, s.bits,
+                             s.group)
+        h = ctypes.c_void_p()
+        assert lib.moe_create(ctypes.byref(cfg), ctypes.byref(h)) == 0
+        n = ctypes.c_size_t()
+        assert lib.moe_workspace_size(h, T, ctypes.byref(n)) == 0
+        lib.moe_destroy(h)
+        dense_h = 2 * (s.num_experts + s.num_shared) * T * s.d_ff
+        assert bench.dense_decode(s) == (n.value >= dense_h), (name, T, n.value, dense_h)
+    assert bench.dense_decode(synth.case_shape("mixtral_decode"))
+    assert not bench.dense_decode(synth.case_shape("fine_decode"))

@@ -145,7 +145,7 @@ def test_out_of_range_shared_slot_sets_flag_and_contributes_zero(T):
     np.testing.assert_allclose(ref["out"], routed_only, rtol=0, atol=0)
 
 
-@pytest.mark.parametrize("name,T", [("fine_tiny", 16), ("fine_tiny", 300), ("tiny_q8g128", 300)])
+@pytest.mark.parametrize("name,T", [("fine_tiny", 16), ("fine_tiny", 300), ("tiny_q8g128", 300), ("tiny", 16)])
 def test_deterministic_and_slot_permutation_invariant(name, T):
     require_gpu()
     case = synth.make_case(name, T=T)
@@ -400,3 +400,90 @@ def test_layers_graph_at_the_benchmarked_decode_shape_matches_the_oracle():
         else:
             np.testing.assert_array_equal(o.cpu().view(torch.int16).numpy(), before[i], err_msg=f"layer {i}")
             assert_out_close(bf16_bits_to_f64(o), ref["out"], what=f"layer {i} after the rewrite")
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 14), ("tiny", 15), ("tiny_q4g128", 16), ("tiny_q8", 16),
+                                    ("tiny_q8g128", 16)])
+def test_dense_tiles_formats_and_ragged_tokens(name, T):
+    """Few tokens with nearly every expert routed to run dense tiles (every
+    expert takes all T tokens; the router runs beside the gate/up GEMM):
+    ragged T, the grouped and 8-bit formats, a shared expert (tiny_q8g128)."""
+    require_gpu()
+    import bench
+    case = synth.make_case(name, T=T)
+    assert bench.dense_decode(case.shape)
+    say(f"{name}: dense tiles, T={T}")
+    res = gpu_layer(case).run(case.hidden)
+    ref = _oracle(case)
+    check_routing(res, ref)
+    assert res["flags"] == 0
+    assert_out_close(res["out"], ref["out"])
+
+
+def test_dense_tiles_with_shared_experts_and_k_equal_e():
+    require_gpu()
+    import bench
+    for shape in (synth.LayerShape(16, 128, 256, 8, 2, 11, "sparse", 0.0, 2),
+                  synth.LayerShape(16, 128, 256, 4, 4, 4, "identity", 0.0, 0)):
+        w = synth.make_weights(shape, seed=7)
+        x = synth.make_hidden(16, 128, seed=7)
+        case = synth.Case("dense", shape, 7, x, w)
+        assert bench.dense_decode(shape)
+        say(f"dense: E={shape.num_experts} k={shape.top_k} shared={shape.num_shared}")
+        res = GpuLayer(shape, w).run(x)
+        ref = _oracle(case)
+        check_routing(res, ref)
+        assert_out_close(res["out"], ref["out"])
+
+
+def test_dense_tiles_flag_only_routed_experts_with_bad_slots():
+    """Dense tiles compute every expert's gate/up before the routing is known;
+    an expert nobody routes to may have an invalid slot (e.g. not resident in
+    the expert cache) without raising the flag, while a routed one raises it
+    and contributes zero."""
+    require_gpu()
+    case = synth.make_case("tiny")
+    E = case.shape.num_experts
+    bias = np.zeros(E, np.float32)
+    bias[7] = -50.0                          # expert 7: never routed to
+    table = case.weights.slot_table.copy()
+    table[7] = -1
+    say("tiny dense: unrouted expert with slot -1")
+    res = gpu_layer(case).run(case.hidden, slot_table=table, router_b=bias)
+    ref = _oracle(case, slot_table=table, router_b=bias)
+    assert ref["counts"][7] == 0
+    assert res["flags"] == 0
+    check_routing(res, ref)
+    assert_out_close(res["out"], ref["out"])
+    bias[2] = 50.0                           # expert 2: every token's first choice, at a bad slot
+    table[2] = 1000
+    say("tiny dense: routed expert at slot 1000")
+    res = gpu_layer(case).run(case.hidden, slot_table=table, router_b=bias)
+    ref = _oracle(case, slot_table=table, router_b=bias)
+    assert ref["counts"][2] == 16
+    assert res["flags"] & 1
+    check_routing(res, ref)
+    assert_out_close(res["out"], ref["out"])
+
+
+def test_one_workspace_across_dense_and_routed_plans():
+    """The same workspace through dense-tile (T = 14..16) and routed-tile
+    plans: every call leaves the control words zero and matches the oracle."""
+    torch = require_gpu()
+    import bench
+    from gpu_util import bf16_bits_to_f64
+    case0 = synth.make_case("tiny")
+    g = gpu_layer(case0)
+    ws = g.layer.new_workspace(300)
+    kinds = set()
+    for T in (16, 5, 14, 64, 16, 300, 15, 1, 16):
+        case = synth.make_case("tiny", T=T)
+        kinds.add(bench.dense_decode(case.shape))
+        say(f"tiny: shared workspace, T={T}")
+        out = g.layer.forward(g.hidden(case.hidden), g.router_w, g.router_b, g.slot_table, g.dw, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:g.layer.control_bytes()].abs().sum().item()) == 0, f"control words not cleared after T={T}"
+        ref = _oracle(case)
+        assert_out_close(bf16_bits_to_f64(out), ref["out"])
+        np.testing.assert_array_equal(g.layer.routing(ws, T)["topk_idx"].cpu().numpy(), ref["topk_idx"])
+    assert kinds == {True, False}
