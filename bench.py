@@ -52,11 +52,12 @@ STREAM_MAX_TOKENS = 64   # the library's decode (weight-streaming) family runs u
 
 def dense_decode(shape) -> bool:
     """Whether the library runs dense tiles for this shape (the rule of its
-    plan): at most 16 tokens, and an expert left without routed rows rare --
-    (1 - k/E)^T <= 0.02 over the routed experts -- and T E <= 1024.  The router
-    then runs in the gate/up launch."""
+    plan): per-row int4 weights, at most 16 tokens, and an expert left without
+    routed rows rare -- (1 - k/E)^T <= 0.02 over the routed experts -- and
+    T E <= 1024.  The router then runs in the gate/up launch."""
     T, E, k = shape.T, shape.num_experts, shape.top_k
-    return 0 < T <= 16 and (1.0 - k / E) ** T <= 0.02 and T * E <= 1024
+    return (shape.bits == 4 and not shape.group and 0 < T <= 16 and (1.0 - k / E) ** T <= 0.02
+            and T * E <= 1024)
 
 
 def kernel_of_stage(stage, T, dense=False):

@@ -149,7 +149,10 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   {
     const int kr = c.top_k - c.num_shared;
     const double idle = std::pow(1.0 - (double)kr / Er, (double)T);
-    p->dense = T <= kStreamTileRows && T <= kStreamMaxTokens && idle <= MOE_DENSE_IDLE_MAX && T * Er <= 1024;
+    // (per-row int4 only: the fused kernel of the other formats spills registers)
+    const bool fits = T <= kStreamTileRows && T <= kStreamMaxTokens && T * Er <= 1024 && c.weight_bits == 4 &&
+                      c.group_size == 0;
+    p->dense = fits && idle <= MOE_DENSE_IDLE_MAX;
   }
   // split the down projection's k range until the grid has enough blocks
   if (p->family == GemmFamily::kStream) {

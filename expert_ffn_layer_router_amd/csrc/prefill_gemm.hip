@@ -53,6 +53,9 @@ constexpr int kQGroup = 128;            // k per (s, z) group of the grouped for
 #ifndef MOE_PF_GU_HANDOVER
 #define MOE_PF_GU_HANDOVER 1
 #endif
+#ifndef MOE_PF_DN_BK4
+#define MOE_PF_DN_BK4 64   // k per stage of the int4 down blocks
+#endif
 #ifndef MOE_PF_DN_STAGES
 #define MOE_PF_DN_STAGES 2
 #endif
@@ -702,7 +705,7 @@ void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& 
     constexpr bool G = decltype(grouped)::value;
     if (c.d_model % (64 * MOE_PF_DN_NJ) == 0) {
       prefill_gemm_kernel<false, MOE_PF_DN_NJ, kPrefillDownStages, kPrefillDownBlocks, MOE_PF_DN_WN,
-                          kPrefillDownWaves, B, G, 64>
+                          kPrefillDownWaves, B, G, (B == 4 ? MOE_PF_DN_BK4 : 64)>
           <<<dim3(c.d_model / (64 * MOE_PF_DN_NJ), p.max_tiles), 64 * kPrefillDownWaves, 0, s>>>(a);
     } else {
       prefill_gemm_kernel<false, 2, 2, 2, 2, 4, B, G, 64><<<dim3(c.d_model / 128, p.max_tiles), 256, 0, s>>>(a);

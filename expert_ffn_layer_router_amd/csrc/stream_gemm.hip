@@ -453,9 +453,6 @@ __device__ __forceinline__ void stream_gemm_body(const StreamArgs& a, int bx, in
     // made the compiler wait for every load in flight, the poll and the next
     // stage's weight copies included.
     u32x4 aset0[RG][KS], aset1[RG][KS];
-    load_a(0, aset0);
-    issue_w(0);
-    if (NBUF == 3 && nst > 1) issue_w(1);
     // Dense tiles: until the router publishes the expert's token mask, tile
     // row r is token r for every r; once a wave sees the mask it loads only
     // the routed tokens' rows (the other lanes repeat the first routed row, so
@@ -473,25 +470,35 @@ __device__ __forceinline__ void stream_gemm_body(const StreamArgs& a, int bx, in
       if constexpr (dense_tile)
         if (lane == 0) load_lds4_coherent(a.tmask + td.x, mask_slots + 4 * (st & 1));
     };
+    // Reads wave 0's poll of the given slot (after a barrier that wave 0
+    // passed once its poll had landed, so every wave reads the same value) and
+    // switches to the routed rows once the mask is known.
+    char* const wave0_slots = smem + NBUF * SBYTES;
+    auto take_mask = [&](int slot) {
+      uint32_t polled = lds_read_b32(wave0_slots + 4 * slot);
+      lds_wait();
+      lds_ready(polled);
+      if (!(known & kMaskKnown) && (polled & kMaskKnown)) {  // block-uniform
+        known = polled;
+        const uint32_t m = known & 0xFFFFu;
+        const int row = ((m >> lr) & 1u) ? lr : (m ? __builtin_ctz(m) : 0);
+        asrc[0] = a.act + (size_t)row * a.d + KR * kp + (KR / 4) * grp;
+      }
+    };
+    load_a(0, aset0);
+    issue_w(0);
+    if (NBUF == 3 && nst > 1) issue_w(1);
     poll(-1);
-    // stage st of the main loop: its fragments are in `use`, stage st + 1's go to `fill`
+    // stage st of the main loop: its fragments are in `use`, stage st + 1's go
+    // to `fill`.  (A block of an expert left without rows runs to the end:
+    // leaving the loop early cost the main loop registers.)
     auto main_stage = [&](int st, const u32x4 (&use)[RG][KS], u32x4 (&fill)[RG][KS]) {
       load_a(st + 1, fill);
       issue_w(st + NBUF - 1);
       poll(st);
       wait_vmem<kPending + (dense_tile ? 1 : 0)>();
-      if constexpr (dense_tile) {
-        uint32_t polled = lds_read_b32(mask_slots + 4 * ((st + 1) & 1));  // the previous poll
-        lds_wait();
-        lds_ready(polled);
-        if (!(known & kMaskKnown) && (polled & kMaskKnown)) {  // wave-uniform
-          known = polled;
-          const uint32_t m = known & 0xFFFFu;
-          const int row = ((m >> lr) & 1u) ? lr : (m ? __builtin_ctz(m) : 0);
-          asrc[0] = a.act + (size_t)row * a.d + KR * kp + (KR / 4) * grp;
-        }
-      }
       lds_barrier();
+      if constexpr (dense_tile) take_mask((st + 1) & 1);  // the previous poll
       compute(st, use);
       lds_barrier();
     };
@@ -595,9 +602,17 @@ __device__ __forceinline__ void stream_gemm_body(const StreamArgs& a, int bx, in
   fused_combine_tail<COLS>(a, bx, ntiles, nz);
 }
 
+#ifndef MOE_STREAM_WPE_DN1
+#define MOE_STREAM_WPE_DN1 7  // 16-row down tiles: 7 blocks per CU (72 VGPRs)
+#endif
+#ifndef MOE_STREAM_WPE_DN2
+#define MOE_STREAM_WPE_DN2 3
+#endif
 template <bool GATEUP, int NCW, int NBUF, int KW, bool NT, int RG, int BITS, bool GROUPED>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(GROUPED ? (RG == 1 ? 3 : 2) : (RG == 1 ? MOE_STREAM_WPE : 3))))
+__attribute__((amdgpu_waves_per_eu(GROUPED ? (RG == 1 ? 3 : 2)
+                                           : (GATEUP ? (RG == 1 ? MOE_STREAM_WPE : 3)
+                                                     : (RG == 1 ? MOE_STREAM_WPE_DN1 : MOE_STREAM_WPE_DN2)))))
 void stream_gemm_kernel(StreamArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[stream_smem_bytes<GATEUP, NCW, NBUF, BITS, GROUPED>()];
   stream_gemm_body<GATEUP, NCW, NBUF, KW, NT, RG, BITS, GROUPED>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z,
@@ -727,19 +742,9 @@ void launch_gateup_router_stream(const moe_config& c, const Plan& p, const uint1
   const int nrouter = r.E * p.small_split;  // T <= 16: one token group
   constexpr int KW = MOE_STREAM_KW_GU;
   constexpr int NCW = MOE_DENSE_NCW;  // per-row formats: blocks of 64 NCW columns
-  if (c.weight_bits == 8) {
-    const dim3 grid(nrouter + c.num_experts * (c.d_ff / (64 * (c.group_size ? 1 : NCW))));
-    if (c.group_size)
-      stream_gemm_router_kernel<1, MOE_STREAM_NBUF, KW, true, 8, true><<<grid, 256, 0, s>>>(a, r, nrouter);
-    else
-      stream_gemm_router_kernel<NCW, MOE_STREAM_NBUF, KW, true, 8, false><<<grid, 256, 0, s>>>(a, r, nrouter);
-  } else {
-    const dim3 grid(nrouter + c.num_experts * (c.d_ff / (64 * (c.group_size ? 1 : NCW))));
-    if (c.group_size)
-      stream_gemm_router_kernel<1, MOE_STREAM_NBUF, KW, true, 4, true><<<grid, 256, 0, s>>>(a, r, nrouter);
-    else
-      stream_gemm_router_kernel<NCW, MOE_STREAM_NBUF, KW, true, 4, false><<<grid, 256, 0, s>>>(a, r, nrouter);
-  }
+  // the plan runs dense tiles for per-row int4 weights only
+  const dim3 grid(nrouter + c.num_experts * (c.d_ff / (64 * NCW)));
+  stream_gemm_router_kernel<NCW, MOE_STREAM_NBUF, KW, true, 4, false><<<grid, 256, 0, s>>>(a, r, nrouter);
 }
 
 void launch_down_stream(const moe_config& c, const Plan& p, const int32_t* slot_table, const moe_weights& w,

@@ -402,16 +402,17 @@ def test_layers_graph_at_the_benchmarked_decode_shape_matches_the_oracle():
             assert_out_close(bf16_bits_to_f64(o), ref["out"], what=f"layer {i} after the rewrite")
 
 
-@pytest.mark.parametrize("name,T", [("tiny", 14), ("tiny", 15), ("tiny_q4g128", 16), ("tiny_q8", 16),
-                                    ("tiny_q8g128", 16)])
-def test_dense_tiles_formats_and_ragged_tokens(name, T):
+@pytest.mark.parametrize("name,T,dense", [("tiny", 14, True), ("tiny", 15, True), ("tiny_q4g128", 16, False),
+                                          ("tiny_q8", 16, False), ("tiny_q8g128", 16, False)])
+def test_dense_tiles_formats_and_ragged_tokens(name, T, dense):
     """Few tokens with nearly every expert routed to run dense tiles (every
-    expert takes all T tokens; the router runs beside the gate/up GEMM):
-    ragged T, the grouped and 8-bit formats, a shared expert (tiny_q8g128)."""
+    expert takes all T tokens; the router runs beside the gate/up GEMM), for
+    per-row int4 weights: ragged T; the grouped and 8-bit formats at the same
+    shapes keep routed tiles (tiny_q8g128 with a shared expert)."""
     require_gpu()
     import bench
     case = synth.make_case(name, T=T)
-    assert bench.dense_decode(case.shape)
+    assert bench.dense_decode(case.shape) == dense
     say(f"{name}: dense tiles, T={T}")
     res = gpu_layer(case).run(case.hidden)
     ref = _oracle(case)
