@@ -51,9 +51,16 @@ __device__ void topk_token(const double* __restrict__ logits, int nsplit, const 
     }
     l[j] = v;
   }
+  // (loops over the k <= 8 rounds are unrolled with guards, so that these
+  // arrays stay in registers: indexed at run time they would live in
+  // scratch memory, which every wave of the kernel would then reserve)
   double best[8];
   int bid[8];
-  for (int r = 0; r < k; ++r) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    best[r] = 0.0;
+    bid[r] = 0;
+    if (r >= k) continue;
     // this lane's best: largest value, lowest id (ids ascend with j)
     double v = 0.0;
     int id = 0x7fffffff;
@@ -82,11 +89,14 @@ __device__ void topk_token(const double* __restrict__ logits, int nsplit, const 
   }
   if (lane == 0) {
     double ex[8], den = 0.0;
-    for (int j = 0; j < k; ++j) {
-      ex[j] = exp(best[j] - best[0]);
-      den += ex[j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ex[j] = j < k ? exp(best[j] - best[0]) : 0.0;
+      if (j < k) den += ex[j];
     }
-    for (int j = 0; j < k; ++j) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= k) continue;
       topk_idx[(size_t)t * kt + j] = bid[j];
       topk_w[(size_t)t * kt + j] = (float)(ex[j] / den);
     }
