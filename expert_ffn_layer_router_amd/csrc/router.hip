@@ -31,31 +31,41 @@ __global__ __launch_bounds__(256) void router_small_kernel(RouterSmallArgs a) {
 // still go to the lower expert id.  A block computes 64 tokens x TN experts
 // over one k-split; each wave 16 tokens x TN experts.  Chunks of 32 k are
 // loaded into registers one chunk ahead, widened to fp64 and stored k-major
-// in LDS, where each MFMA operand is one conflict-free ds_read_b64 (lane l:
-// A = x[t0 + l % 16][k + l / 16], B = W[e0 + l % 16][k + l / 16]; D element
-// r of lane l is (token l / 16 + 4 r, expert l % 16)).  Output:
-// logits[split][t][e], summed in split order by router_topk_kernel.
+// in one of two LDS buffers (the products of one chunk run while the next is
+// stored into the other, one barrier per chunk), where each MFMA operand is
+// one conflict-free ds_read_b64 (lane l: A = x[t0 + l % 16][k + l / 16],
+// B = W[e0 + l % 16][k + l / 16]; D element r of lane l is (token l / 16 +
+// 4 r, expert l % 16)).  Output: logits[split][t][e], summed in split order
+// by router_topk_kernel.  The blocks of the first expert tile also write
+// their part of x in fragment k-order (xperm, the prefill gate/up GEMM's A
+// operand) and per token the fp64 sum of their k range (xsum_part[split][t],
+// for the GEMM's zero-point term), so x is read from HBM once.
 template <int TN>
 __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t* __restrict__ hidden,
                                                                  const float* __restrict__ wr,
                                                                  double* __restrict__ logits, int T, int d, int E,
-                                                                 int kchunk) {
+                                                                 int kchunk, uint16_t* __restrict__ xperm,
+                                                                 double* __restrict__ xsum_part) {
   constexpr int TM = kRouterMfmaTokens, KC = kRouterMfmaK, NB = TN / 16;
-  __shared__ double xs[KC][TM];
-  __shared__ double wsh[KC][TN];
+  __shared__ double xs[2][KC][TM];
+  __shared__ double wsh[2][KC][TN];
+  __shared__ double srow[4][TM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * TM, e0 = blockIdx.y * TN, split = blockIdx.z;
   const int kbeg = split * kchunk, kend = kbeg + kchunk;
+  const bool xcopy = blockIdx.y == 0;  // this block writes its part of xperm and xsum_part
   // staging: thread -> x row t0 + tid % 64, k 8 (tid / 64) .. +8 of the chunk;
   // W row e0 + tid % TN (the first 4 TN threads: 8 k each)
   const int xr = tid % TM, xk = 8 * (tid / TM);
   const bool xok = t0 + xr < T;
   const uint16_t* xsrc = hidden + (size_t)(xok ? t0 + xr : 0) * d + xk;
+  uint16_t* xdst = xperm + (size_t)(xok ? t0 + xr : 0) * d + xk;
   const int wrow = tid % TN, wk = 8 * (tid / TN);
   const bool wact = tid < 4 * TN, wok = wact && e0 + wrow < E;
   const float* wsrc = wr + (size_t)(wok ? e0 + wrow : 0) * d + (wact ? wk : 0);
   u32x4 xv;
   float4 w0, w1;
+  double sx = 0.0;  // this thread's x values, summed
   auto fetch = [&](int kc) {
     xv = *reinterpret_cast<const u32x4*>(xsrc + kc);
     if (wact) {
@@ -63,37 +73,43 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t*
       w1 = *reinterpret_cast<const float4*>(wsrc + kc + 4);
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int buf, int kc) {
     const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xs[xk + 2 * i][xr] = xok ? (double)__uint_as_float(xw[i] << 16) : 0.0;
-      xs[xk + 2 * i + 1][xr] = xok ? (double)__uint_as_float(xw[i] & 0xFFFF0000u) : 0.0;
+      const double lo = (double)__uint_as_float(xw[i] << 16), hi = (double)__uint_as_float(xw[i] & 0xFFFF0000u);
+      xs[buf][xk + 2 * i][xr] = xok ? lo : 0.0;
+      xs[buf][xk + 2 * i + 1][xr] = xok ? hi : 0.0;
+      sx += lo + hi;
     }
+    if (xcopy && xok) *reinterpret_cast<u32x4*>(xdst + kc) = permute_a(xv);
     if (wact) {
       const float wf[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) wsh[wk + i][wrow] = wok ? (double)wf[i] : 0.0;
+      for (int i = 0; i < 8; ++i) wsh[buf][wk + i][wrow] = wok ? (double)wf[i] : 0.0;
     }
   };
   f64x4 acc[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) acc[n] = f64x4{0.0, 0.0, 0.0, 0.0};
   fetch(kbeg);
-  for (int kc = kbeg; kc < kend; kc += KC) {
-    __syncthreads();  // the previous chunk's operands are read
-    stage();
-    __syncthreads();
-    if (kc + KC < kend) fetch(kc + KC);  // next chunk's loads in flight during the products
+  stage(0, kbeg);
+  __syncthreads();
+  for (int kc = kbeg, buf = 0; kc < kend; kc += KC, buf ^= 1) {
+    const bool more = kc + KC < kend;
+    if (more) fetch(kc + KC);  // next chunk's loads in flight during the products
 #pragma unroll
     for (int k4 = 0; k4 < KC; k4 += 4) {
-      const double av = xs[k4 + lane / 16][16 * wave + lane % 16];
+      const double av = xs[buf][k4 + lane / 16][16 * wave + lane % 16];
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        const double bv = wsh[k4 + lane / 16][16 * n + lane % 16];
+        const double bv = wsh[buf][k4 + lane / 16][16 * n + lane % 16];
         acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[n], 0, 0, 0);
       }
     }
+    // the other buffer was last read before the previous barrier
+    if (more) stage(buf ^ 1, kc + KC);
+    __syncthreads();
   }
 #pragma unroll
   for (int n = 0; n < NB; ++n)
@@ -102,30 +118,33 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t*
       const int t = t0 + 16 * wave + lane / 16 + 4 * r, e = e0 + 16 * n + lane % 16;
       if (t < T && e < E) logits[((size_t)split * T + t) * E + e] = acc[n][r];
     }
+  if (xcopy) {  // the four threads of each row, in a fixed order
+    srow[tid / TM][xr] = sx;
+    __syncthreads();
+    if (tid < TM && t0 + tid < T)
+      xsum_part[(size_t)split * T + t0 + tid] = ((srow[0][tid] + srow[1][tid]) + srow[2][tid]) + srow[3][tid];
+  }
 }
 
+// One wave per token: the top-k (topk_token) and the row sum of x for the
+// gate/up GEMM's zero-point term (the logits kernel's per-split sums, added
+// in split order).
 __global__ __launch_bounds__(256) void router_topk_kernel(const double* __restrict__ logits, int nsplit,
-                                                          const float* __restrict__ bias,
-                                                          const uint16_t* __restrict__ hidden, int d, int T,
-                                                          int E, int k, int ns, int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_w, float* __restrict__ xsum,
-                                                          uint16_t* __restrict__ xperm, uint32_t* __restrict__ flags) {
+                                                          const float* __restrict__ bias, int T, int E, int k,
+                                                          int ns, int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w,
+                                                          const double* __restrict__ xsum_part,
+                                                          float* __restrict__ xsum, uint32_t* __restrict__ flags) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
-  topk_token<false>(logits, nsplit, bias, T, E, k, ns, t, lane, topk_idx, topk_w);
-  // row sum of x (for the gate/up GEMM's zero-point term) and x in fragment
-  // k-order (the gate/up GEMM's A operand then needs no permutes)
+  // the row sum's parts, loaded first (lane l: splits l, l + 64, ...) so that
+  // their latency overlaps the top-k; summed lane by lane, then across the
+  // lanes by a butterfly (a fixed order: the sum is rounded to fp32 anyway)
   double sx = 0.0;
-  for (int kk = lane * 8; kk < d; kk += 512) {
-    const u32x4 xv = *reinterpret_cast<const u32x4*>(hidden + (size_t)t * d + kk);
-    *reinterpret_cast<u32x4*>(xperm + (size_t)t * d + kk) = permute_a(xv);
-    const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sx += (double)__uint_as_float(xs[i] << 16) + (double)__uint_as_float(xs[i] & 0xFFFF0000u);
-  }
+  for (int s = lane; s < nsplit; s += 64) sx += xsum_part[(size_t)s * T + t];
+  topk_token<false>(logits, nsplit, bias, T, E, k, ns, t, lane, topk_idx, topk_w);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sx += __shfl_xor(sx, off, 64);
   if (lane == 0) xsum[t] = (float)sx;
@@ -171,16 +190,19 @@ void launch_router(const moe_config& c, const Plan& p, const uint16_t* hidden, c
   const int tn = router_tile_experts(E);
   dim3 grid((p.T + kRouterMfmaTokens - 1) / kRouterMfmaTokens, (E + tn - 1) / tn, p.router_split);
   const int kchunk = c.d_model / p.router_split;
+  uint16_t* xperm = reinterpret_cast<uint16_t*>(ws + p.xperm);
+  double* xsum_part = reinterpret_cast<double*>(ws + p.xsum_part);
   if (tn == 64)
-    router_logits_mfma_kernel<64><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, E, kchunk);
+    router_logits_mfma_kernel<64><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, E, kchunk, xperm,
+                                                       xsum_part);
   else if (tn == 32)
-    router_logits_mfma_kernel<32><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, E, kchunk);
+    router_logits_mfma_kernel<32><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, E, kchunk, xperm,
+                                                       xsum_part);
   else
-    router_logits_mfma_kernel<16><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, E, kchunk);
-  router_topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(logits, p.router_split, router_bias, hidden, c.d_model, p.T,
-                                                   E, k, ns, topk_idx, topk_w,
-                                                   reinterpret_cast<float*>(ws + p.xsum),
-                                                   reinterpret_cast<uint16_t*>(ws + p.xperm), flags);
+    router_logits_mfma_kernel<16><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, E, kchunk, xperm,
+                                                       xsum_part);
+  router_topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(logits, p.router_split, router_bias, p.T, E, k, ns, topk_idx,
+                                                   topk_w, xsum_part, reinterpret_cast<float*>(ws + p.xsum), flags);
 }
 
 }  // namespace moe

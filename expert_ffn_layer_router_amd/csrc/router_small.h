@@ -40,14 +40,21 @@ __device__ void topk_token(const double* __restrict__ logits, int nsplit, const 
     live[j] = e < E;
     double v = 0.0;
     if (live[j]) {
-      if (kCoherent) {
-        v = load_coherent(&logits[(size_t)t * E + e]);
-        for (int s = 1; s < nsplit; ++s) v += load_coherent(&logits[((size_t)s * T + t) * E + e]);
-      } else {
-        v = logits[(size_t)t * E + e];
-        for (int s = 1; s < nsplit; ++s) v += logits[((size_t)s * T + t) * E + e];
+      // the splits in order, then the bias; eight loads in flight at a time
+      // (a missing split adds +0.0, which changes no sum)
+      const double bv = bias ? (double)bias[e] : 0.0;
+      auto ld = [&](int s) {
+        const double* q = &logits[((size_t)s * T + t) * E + e];
+        return kCoherent ? load_coherent(q) : *q;
+      };
+      for (int s0 = 0; s0 < nsplit; s0 += 8) {
+        double p[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) p[u] = s0 + u < nsplit ? ld(s0 + u) : 0.0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v += p[u];
       }
-      if (bias) v += (double)bias[e];
+      if (bias) v += bv;
     }
     l[j] = v;
   }
@@ -87,19 +94,28 @@ __device__ void topk_token(const double* __restrict__ logits, int nsplit, const 
     for (int j = 0; j < kPer; ++j)
       if (lane + 64 * j == id) live[j] = false;
   }
+  // lane j < k takes choice j: exp(l_j - l_0) in parallel, then the sum in
+  // order j = 0 .. k-1 (every lane forms the same sum)
+  double bj = best[0];
+  int ij = bid[0];
+#pragma unroll
+  for (int r = 1; r < 8; ++r)
+    if (lane == r) {
+      bj = best[r];
+      ij = bid[r];
+    }
+  const double ex = lane < k ? exp(bj - best[0]) : 0.0;
+  double den = 0.0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const double ej = __shfl(ex, j, 64);
+    if (j < k) den += ej;
+  }
+  if (lane < k) {
+    topk_idx[(size_t)t * kt + lane] = ij;
+    topk_w[(size_t)t * kt + lane] = (float)(ex / den);
+  }
   if (lane == 0) {
-    double ex[8], den = 0.0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      ex[j] = j < k ? exp(best[j] - best[0]) : 0.0;
-      if (j < k) den += ex[j];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= k) continue;
-      topk_idx[(size_t)t * kt + j] = bid[j];
-      topk_w[(size_t)t * kt + j] = (float)(ex[j] / den);
-    }
     for (int j = 0; j < ns; ++j) {
       topk_idx[(size_t)t * kt + k + j] = E + j;
       topk_w[(size_t)t * kt + k + j] = 1.0f;
