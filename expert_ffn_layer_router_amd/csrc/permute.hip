@@ -19,7 +19,8 @@
 namespace moe {
 
 __global__ __launch_bounds__(kPermuteThreads) void permute_kernel(RegroupArgs a) {
-  regroup_block<kPermuteThreads>(a);
+  __shared__ __attribute__((aligned(16))) char lds[regroup_lds_bytes<kPermuteThreads>()];
+  regroup_block<kPermuteThreads>(a, lds);
 }
 
 // Many rows: the same regroup over chunks of kPermuteThreads assignments, one

@@ -18,19 +18,25 @@ struct RegroupArgs {
   int32_t* num_tiles;
 };
 
-// Runs on one workgroup of NT threads (a multiple of 64, <= 1024).  Callers
-// make earlier global writes of topk_idx visible to the block first.
+// LDS bytes regroup_block<NT> works in.
 template <int NT>
-__device__ void regroup_block(const RegroupArgs& a) {
+constexpr int regroup_lds_bytes() { return (3 + NT / 64) * 256 * 4; }
+
+// Runs on one workgroup of NT threads (a multiple of 64, <= 1024).  Callers
+// make earlier global writes of topk_idx visible to the block first.  lds:
+// regroup_lds_bytes<NT>() bytes of LDS the block does not otherwise use
+// meanwhile, 4-byte aligned.
+template <int NT>
+__device__ void regroup_block(const RegroupArgs& a, char* lds) {
   constexpr int NW = NT / 64;
-  __shared__ int cnt[256];
-  __shared__ int base[256];
-  __shared__ int wc[NW][256];
+  int* cnt = reinterpret_cast<int*>(lds);  // [256] rows per expert
+  int* base = cnt + 256;                   // [256] running grouped position per expert
+  int* tstart = base + 256;                // [256] first row tile per expert
+  int (*wc)[256] = reinterpret_cast<int (*)[256]>(tstart + 256);  // [NW][256] per-wave counts
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int R = a.R, E = a.E;
 
-  __shared__ int tstart[256];
   for (int e = tid; e < E; e += NT) cnt[e] = 0;
   __syncthreads();
   for (int i = tid; i < R; i += NT) atomicAdd(&cnt[a.topk_idx[i]], 1);

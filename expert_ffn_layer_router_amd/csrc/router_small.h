@@ -145,10 +145,10 @@ constexpr uint32_t kMaskKnown = 0x80000000u;
 
 // LDS the body needs for a finish that stages up to MAX_TE logits of at most
 // MAX_T tokens: per-wave partials and the ticket flag, then the logits, bias,
-// slots and chosen ids.
+// slots and chosen ids, then the regroup's working space.
 template <int MAX_TE, int MAX_T>
 constexpr int router_small_lds_bytes() {
-  return 4 * kRouterTokTile * 8 + 16 + (MAX_TE + 1) * 8 + 256 * 8 + 256 * 4 + MAX_T * 8 * 4;
+  return 4 * kRouterTokTile * 8 + 16 + (MAX_TE + 1) * 8 + 256 * 8 + 256 * 4 + MAX_T * 8 * 4 + regroup_lds_bytes<256>();
 }
 
 // One block of the few-token router: expert e, tokens t0 .. t0+15 (fewer at
@@ -169,6 +169,7 @@ __device__ void router_small_body(const RouterSmallArgs& a, int e, int t0, int z
   double* sbias = lg + MAX_TE + 1;
   int32_t* sslot = reinterpret_cast<int32_t*>(sbias + 256);
   int32_t* sid = sslot + 256;
+  char* rg_lds = reinterpret_cast<char*>(sid + MAX_T * 8);  // the regroup's working space
   const int T = a.T, d = a.d, E = a.E, k = a.k, ns = a.ns;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nt = min(kRouterTokTile, T - t0);
@@ -333,14 +334,14 @@ __device__ void router_small_body(const RouterSmallArgs& a, int e, int t0, int z
     RegroupArgs la = ra;
     la.topk_idx = sid;
     la.slot_table = sslot;
-    regroup_block<256>(la);
+    regroup_block<256>(la, rg_lds);
     if (threadIdx.x == 0) reset_ticket(a.ticket);
     return;
   }
   for (int t = wave; t < T; t += 4)
     topk_token<true>(a.logits, nsplit, a.bias, T, E, k, ns, t, lane, a.topk_idx, a.topk_w);
   __syncthreads();
-  regroup_block<256>(ra);
+  regroup_block<256>(ra, rg_lds);
   if (threadIdx.x == 0) reset_ticket(a.ticket);
 }
 
