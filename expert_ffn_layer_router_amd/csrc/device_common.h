@@ -75,6 +75,16 @@ __device__ __forceinline__ u32x4 codes_to_bf16(uint32_t w) {
   return r;
 }
 
+// The same with the mask and bias given (zero for both gives zeros).
+__device__ __forceinline__ u32x4 codes_to_bf16_masked(uint32_t w, uint32_t mask, uint32_t bias) {
+  u32x4 r;
+  r.x = (w & mask) | bias;
+  r.y = ((w >> 4) & mask) | bias;
+  r.z = ((w >> 8) & mask) | bias;
+  r.w = ((w >> 12) & mask) | bias;
+  return r;
+}
+
 // 8-bit codes on the load path: bytes k0..k3 in w0 and k4..k7 in w1 -> the
 // bf16 pairs (k0, k4), (k1, k5), (k2, k6), (k3, k7), the fragment k-order
 // above.  A code 0..255 has at most 8 significant bits, so it converts to
@@ -94,23 +104,14 @@ __device__ __forceinline__ u32x4 bytes_to_bf16(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-// Codes to bf16(q f + m), in the fragment order of codes_to_bf16 /
-// bytes_to_bf16 (the conversion rounds to nearest even).  With f = 1 and
-// m = -z (integer z) this is q - z, exact: |q - z| <= 255 has at most 8
-// significant bits; f = 0, m = 0 gives zeros.
+// 8-bit codes to bf16(q f + m), in the fragment order of bytes_to_bf16 (the
+// conversion rounds to nearest even).  With f = 1 and m = -z (integer z)
+// this is q - z, exact: |q - z| <= 255 has at most 8 significant bits; f = 0,
+// m = 0 gives zeros.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
-}
-__device__ __forceinline__ u32x4 dequant_int4_bf16(uint32_t w, float s, float m) {
-  const uint32_t t0 = w & 0x0F0F0F0Fu, t1 = (w >> 4) & 0x0F0F0F0Fu;  // k0 k2 k4 k6 / k1 k3 k5 k7
-  u32x4 r;
-  r.x = pack_bf16_rne(fmaf(code_byte_f32(t0, 0), s, m), fmaf(code_byte_f32(t0, 2), s, m));  // (k0, k4)
-  r.y = pack_bf16_rne(fmaf(code_byte_f32(t1, 0), s, m), fmaf(code_byte_f32(t1, 2), s, m));  // (k1, k5)
-  r.z = pack_bf16_rne(fmaf(code_byte_f32(t0, 1), s, m), fmaf(code_byte_f32(t0, 3), s, m));  // (k2, k6)
-  r.w = pack_bf16_rne(fmaf(code_byte_f32(t1, 1), s, m), fmaf(code_byte_f32(t1, 3), s, m));  // (k3, k7)
-  return r;
 }
 __device__ __forceinline__ u32x4 dequant_int8_bf16(uint32_t w0, uint32_t w1, float s, float m) {
   u32x4 r;

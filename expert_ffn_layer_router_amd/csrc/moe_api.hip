@@ -196,6 +196,10 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   p->xperm = take(p->family == GemmFamily::kPrefill ? 2 * (size_t)T * c.d_model : 0);
   // prefill: per k-split fp64 row sums of x (the router's logits kernel writes them)
   p->xsum_part = take(p->family == GemmFamily::kPrefill ? 8 * (size_t)p->router_split * T : 0);
+  // prefill, grouped int4 weights: sums of x per token and group of 128 k
+  p->xgsum = take(p->family == GemmFamily::kPrefill && c.group_size && c.weight_bits == 4
+                      ? 4 * (size_t)T * (c.d_model / 128)
+                      : 0);
   // many rows: per-chunk expert histograms of the regroup
   p->rhist = take(p->family == GemmFamily::kPrefill ? 4 * (size_t)((p->R + kPermuteThreads - 1) / kPermuteThreads) * E : 0);
   p->total = off;

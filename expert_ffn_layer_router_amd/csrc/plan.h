@@ -62,7 +62,7 @@ struct Plan {
   // words that must be zero before first use and are left zero by every call
   size_t ctrl = 0, ctrl_bytes = 0, tmask = 0, flags = 0, logits = 0, topk_idx = 0, topk_w = 0, counts = 0,
          offsets = 0, perm = 0, inv = 0, tiles = 0, num_tiles = 0, xsum = 0, hsum_part = 0, h = 0, y = 0,
-         xperm = 0, xsum_part = 0, rhist = 0, total = 0;
+         xperm = 0, xsum_part = 0, xgsum = 0, rhist = 0, total = 0;
 };
 
 // Fills `p` for T tokens.  Pure host arithmetic.

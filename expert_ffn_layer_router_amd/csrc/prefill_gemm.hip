@@ -130,8 +130,12 @@ struct PrefillArgs {
   const int4* tiles;
   const int32_t* num_tiles;
   const float* xsum;          // gate/up: [T] row sums of hidden
-  float* hsum_part;           // gate/up writes, down reads: [R][hparts]
-  int hparts;                 // gate/up column blocks (partial h row sums per row)
+  float* hsum_part;           // gate/up writes, down reads: [R][hparts] sums of h per 128 columns
+  int hparts;                 // dff / 128
+  // grouped formats: per row and 128-k group, the sum of A over the group
+  // (gate/up: [T][d / 128] of hidden, by token; down: hsum_part)
+  const float* gsum;
+  int gsum_stride;
   int num_slots, d, dff, topk;
   const uint8_t* w0;          // gate (or down) codes
   const uint8_t* w1;          // up codes
@@ -154,13 +158,19 @@ struct PrefillArgs {
 // row).  Per-row formats widen the codes exactly and apply (s, z) in the
 // epilogue.  GROUPED (one (s, z) per output row and 128-k group): every
 // stage also copies the (s, z) of its group for the block's weight rows into
-// LDS; the codes are widened to q - z (exact in bf16: at most 8 significant
-// bits), and each accumulator is kept in units of its column's current group
+// LDS, and each accumulator is kept in units of its column's current group
 // scale: at a group boundary it is multiplied by s_old / s_new (one fp32
-// rounding per group), and the epilogue multiplies by the last scale.  So
-// every weight enters the matrix cores exactly and no second set of
-// accumulators is needed.  A zero scale zeroes its group's codes and keeps
-// the previous scale.
+// rounding per group); the epilogue multiplies by the last scale.  A zero
+// scale zeroes its group's terms and keeps the previous scale.  The
+// zero-point z:
+//  - int4: the codes are widened as for the per-row formats (128 + q, exact),
+//    the stage also copies, for the block's rows, the sum S of A over the
+//    group (precomputed), and the group's offset term -(128 + z) S enters
+//    through one more matrix-core product per accumulator: S split into
+//    three bf16 parts (about 24 significant bits) against -(128 + z) (exact
+//    in bf16).  Cheaper in vector instructions than widening to q - z;
+//  - 8-bit: the codes are widened to q - z (exact in bf16: at most 8
+//    significant bits).  (The offset product measured slower here.)
 template <bool GATEUP, int NJ, int kNBuf, int OCC, int WN, int NW, int BITS, bool GROUPED, int kBK>
 __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs a) {
   static_assert(BITS == 4 || BITS == 8, "int4 or 8-bit codes");
@@ -178,7 +188,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
   // copies (4 bytes per lane), kPI per wave
   constexpr int kPI = GROUPED ? (4 * kWRows + 256 * NW - 1) / (256 * NW) : 0;
   constexpr int kPBytes = kPI * 256 * NW;
-  constexpr int kStage = kABytes + kWBytes + kPBytes;
+  // grouped: the group sums S of the block's rows, one 256-byte copy (4 bytes
+  // per lane) per wave, row (64 wave + lane) mod 128
+  constexpr bool kOffsetMfma = GROUPED && BITS == 4;  // int4 grouped: the offset term as a product
+  constexpr int kGI = kOffsetMfma ? 1 : 0;
+  constexpr int kGBytes = kGI * 256 * NW;
+  constexpr int kStage = kABytes + kWBytes + kPBytes + kGBytes;
   constexpr int kAI = (kABytes / 1024) / NW;  // activation-load instructions (1 KB) per wave per stage
   constexpr int kWI = (kWBytes / 1024) / NW;  // weight-load instructions per wave per stage
   constexpr float kBias = code_bias<BITS>();
@@ -256,6 +271,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
       psrc[q] = reinterpret_cast<const uint8_t*>(arr + (size_t)slot * ngroups * ncols + n);
     }
   }
+  // grouped: this lane's row of the group sums
+  const float* gsrc = nullptr;
+  if constexpr (kOffsetMfma) {
+    const int r = (64 * wave + lane) % kBM;
+    const int rr = r < rows ? r : 0;
+    const int grow = GATEUP ? a.perm[pbase + rr] / a.topk : pbase + rr;
+    gsrc = a.gsum + (size_t)grow * a.gsum_stride;
+  }
   // row sums of A for the zero-point term
   if (tid < kBM) {
     float v = 0.0f;
@@ -289,6 +312,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
       for (int q = 0; q < kPI; ++q)
         load_lds4(psrc[q] + (size_t)(st * kBK / kQGroup) * ncols * 2, buf + kABytes + kWBytes + (q * NW + wave) * 256);
+      if constexpr (kOffsetMfma) load_lds4(gsrc + st * kBK / kQGroup, buf + kABytes + kWBytes + kPBytes + wave * 256);
     }
   };
 
@@ -306,11 +330,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
     wr[j] = GATEUP ? (j < HJ ? 32 * HJ * wn + 32 * j : kWRows / 2 + 32 * HJ * wn + 32 * (j - HJ)) : 32 * NJW * wn + 32 * j;
 
   // grouped formats: per weight-row block of this wave, the scale its sums
-  // are kept in, and the current group's code factor (1, or 0 for a zero
-  // scale) and offset (-z times it)
+  // are kept in; int4: the current group's code mask and bias (zero for a
+  // zero scale); 8-bit: its code factor (1, or 0 for a zero scale) and
+  // offset (-z times it)
   float cur_s[NJW], gf[NJW], gm[NJW];
+  uint32_t gmask[NJW], gbias[NJW];
 #pragma unroll
-  for (int j = 0; j < NJW; ++j) cur_s[j] = gf[j] = 1.0f, gm[j] = 0.0f;
+  for (int j = 0; j < NJW; ++j) cur_s[j] = gf[j] = 1.0f, gm[j] = 0.0f, gmask[j] = gbias[j] = 0u;
 
   // row blocks of 32 of this wave that hold rows of the tile (the rest are
   // skipped: a tile's last rows may be missing)
@@ -330,9 +356,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
       // past stage st - 1, so its buffer can be refilled with stage st + kNBuf - 1
       const int later = min(kNBuf - 2, nst - 1 - st);
       if (kNBuf > 3 && later >= 2)
-        wait_vmem<(kNBuf > 3 ? 2 : 0) * (kAI + kWI + kPI)>();
+        wait_vmem<(kNBuf > 3 ? 2 : 0) * (kAI + kWI + kPI + kGI)>();
       else if (kNBuf > 2 && later >= 1)
-        wait_vmem<(kNBuf > 2 ? 1 : 0) * (kAI + kWI + kPI)>();
+        wait_vmem<(kNBuf > 2 ? 1 : 0) * (kAI + kWI + kPI + kGI)>();
       else
         wait_vmem<0>();
       lds_barrier();
@@ -350,7 +376,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
                                                      16 * spos<kCPR>(r, (kCPR / 2) * hh + c));
       }
       if constexpr (GROUPED) {
-        if ((st * kBK) % kQGroup == 0) {  // first stage of a group: its (s, z), rescale the sums
+        if ((st * kBK) % kQGroup == 0 && !kOffsetMfma) {  // 8-bit: first stage of a group
           const uint16_t* pz = reinterpret_cast<const uint16_t*>(buf + kABytes + kWBytes);
 #pragma unroll
           for (int j = 0; j < NJW; ++j) {
@@ -366,18 +392,52 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
               if (i < ML) acc[i][j] *= rho;
           }
         }
+        if ((st * kBK) % kQGroup == 0 && kOffsetMfma) {
+          // int4: first stage of a group: its (s, z); rescale the sums, then
+          // add the group's offset term -(128 + z) S as one product per
+          // accumulator (A: S in three bf16 parts at k 0..2 of the lanes of
+          // k-group 0; B: -(128 + z) at the same k; the rest zero)
+          const uint16_t* pz = reinterpret_cast<const uint16_t*>(buf + kABytes + kWBytes);
+          const float* gs = reinterpret_cast<const float*>(buf + kABytes + kWBytes + kPBytes);
+          u32x4 sa[MI];
+#pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            const float sv = gs[32 * MI * wm + 32 * i + l32];
+            const uint16_t h0 = f32_to_bf16(sv);
+            const float r1 = sv - bf16_to_f32(h0);
+            const uint16_t h1 = f32_to_bf16(r1);
+            const uint16_t h2 = f32_to_bf16(r1 - bf16_to_f32(h1));
+            sa[i] = hh == 0 ? u32x4{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2, 0u, 0u}
+                            : u32x4{0u, 0u, 0u, 0u};
+          }
+#pragma unroll
+          for (int j = 0; j < NJW; ++j) {
+            const int r = wr[j] + l32;
+            const float sj = fp16_to_f32(pz[r]), zj = fp16_to_f32(pz[kWRows + r]);
+            const bool live = sj != 0.0f;
+            const float rho = live ? cur_s[j] / sj : 1.0f;
+            cur_s[j] = live ? sj : cur_s[j];
+            gmask[j] = live ? 0x000F000Fu : 0u;
+            gbias[j] = live ? 0x43004300u : 0u;
+            const uint32_t nc = live ? (uint32_t)f32_to_bf16(-(kBias + zj)) : 0u;  // exact: an integer below 2^8
+            const u32x4 sb = hh == 0 ? u32x4{nc | (nc << 16), nc, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+              if (i < ML) acc[i][j] = mfma32(sa[i], sb, acc[i][j] * rho);
+          }
+        }
       }
       auto widen = [&](int j, int s) {
         const uint32_t w0 = bq[j][(BITS / 4) * s / 4][((BITS / 4) * s) % 4];
         if constexpr (BITS == 4) {
           if constexpr (GROUPED)
-            return dequant_int4_bf16(w0, gf[j], gm[j]);  // q - z, or 0 for a zero scale
+            return codes_to_bf16_masked(w0, gmask[j], gbias[j]);  // bias + q, or 0 for a zero scale
           else
             return codes_to_bf16(w0);
         } else {
           const uint32_t w1 = bq[j][(2 * s + 1) / 4][(2 * s + 1) % 4];
           if constexpr (GROUPED)
-            return dequant_int8_bf16(w0, w1, gf[j], gm[j]);
+            return dequant_int8_bf16(w0, w1, gf[j], gm[j]);  // q - z, or 0 for a zero scale
           else
             return bytes_to_bf16(w0, w1);
         }
@@ -514,7 +574,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
   // The barriers here wait for LDS only: a store has read its data out of LDS
   // once issued, and nothing here reads global memory the stores write.
   lds_barrier();
-  if (GATEUP) {
+  if constexpr (GATEUP) {
     constexpr int kCols = kWRows / 2;  // output columns of the block
     static_assert(kBM * kCols * 2 <= kNBuf * kStage, "h tile fits the stage ring");
     uint16_t* htile = reinterpret_cast<uint16_t*>(smem);  // [kBM][kCols], columns in h_phys_col order
@@ -566,11 +626,17 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
       *reinterpret_cast<u32x4*>(a.h + (size_t)(pbase + r) * a.dff + n0 + 8 * q) =
           *reinterpret_cast<const u32x4*>(htile + r * kCols + 8 * q);
     }
+    // per 128 columns (a group of the grouped formats): the sum of its waves' parts
+    constexpr int kGroups = kCols / kQGroup, kWavesPerGroup = WN / kGroups;
+    static_assert(kGroups * kQGroup == kCols && kWavesPerGroup * 32 * HJ == kQGroup, "whole groups per wave set");
     if (tid < rows && tid < kBM) {
-      float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < WN; ++w) v += hpart[w][tid];
-      a.hsum_part[(size_t)(pbase + tid) * a.hparts + blockIdx.x] = v;
+      for (int g = 0; g < kGroups; ++g) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWavesPerGroup; ++w) v += hpart[g * kWavesPerGroup + w][tid];
+        a.hsum_part[(size_t)(pbase + tid) * a.hparts + blockIdx.x * kGroups + g] = v;
+      }
     }
   } else if constexpr (WM == 1) {
     // one pass per 32-row block: every wave holds all rows of the block
@@ -658,6 +724,8 @@ void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* h
   a.num_tiles = reinterpret_cast<const int32_t*>(ws + p.num_tiles);
   a.xsum = reinterpret_cast<const float*>(ws + p.xsum);
   a.hsum_part = reinterpret_cast<float*>(ws + p.hsum_part);
+  a.gsum = reinterpret_cast<const float*>(ws + p.xgsum);
+  a.gsum_stride = c.d_model / 128;
   a.num_slots = c.num_slots;
   a.d = c.d_model;
   a.dff = c.d_ff;
@@ -670,8 +738,8 @@ void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* h
   a.z1 = w.z_up;
   a.h = reinterpret_cast<uint16_t*>(ws + p.h);
   a.flags = reinterpret_cast<uint32_t*>(ws + p.flags);
-  a.hparts = gateup_blocks(c);
-  dim3 grid(a.hparts, p.max_tiles);
+  a.hparts = c.d_ff / 128;
+  dim3 grid(gateup_blocks(c), p.max_tiles);
   with_format(c, [&](auto bits, auto grouped) {
     constexpr int B = decltype(bits)::value;
     constexpr bool G = decltype(grouped)::value;
@@ -690,7 +758,9 @@ void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& 
   a.tiles = reinterpret_cast<const int4*>(ws + p.tiles);
   a.num_tiles = reinterpret_cast<const int32_t*>(ws + p.num_tiles);
   a.hsum_part = reinterpret_cast<float*>(ws + p.hsum_part);
-  a.hparts = gateup_blocks(c);
+  a.hparts = c.d_ff / 128;
+  a.gsum = a.hsum_part;
+  a.gsum_stride = a.hparts;
   a.num_slots = c.num_slots;
   a.d = c.d_model;
   a.dff = c.d_ff;

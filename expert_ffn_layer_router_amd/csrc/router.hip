@@ -128,13 +128,16 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t*
 
 // One wave per token: the top-k (topk_token) and the row sum of x for the
 // gate/up GEMM's zero-point term (the logits kernel's per-split sums, added
-// in split order).
+// in split order).  Grouped int4 weights (xgsum not null): also the sums of
+// x over each group of 128 k, [T][d / 128].
 __global__ __launch_bounds__(256) void router_topk_kernel(const double* __restrict__ logits, int nsplit,
                                                           const float* __restrict__ bias, int T, int E, int k,
                                                           int ns, int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ topk_w,
                                                           const double* __restrict__ xsum_part,
-                                                          float* __restrict__ xsum, uint32_t* __restrict__ flags) {
+                                                          float* __restrict__ xsum, uint32_t* __restrict__ flags,
+                                                          const uint16_t* __restrict__ hidden, int d,
+                                                          float* __restrict__ xgsum) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -148,6 +151,19 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const double* __restri
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sx += __shfl_xor(sx, off, 64);
   if (lane == 0) xsum[t] = (float)sx;
+  if (xgsum) {
+    // lane l: k = 8 l .. 8 l + 7 of every 512, so 16 lanes cover a group
+    for (int kk = 0; kk < d; kk += 512) {
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(hidden + (size_t)t * d + kk + 8 * lane);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      float g = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g += __uint_as_float(xw[i] << 16) + __uint_as_float(xw[i] & 0xFFFF0000u);
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) g += __shfl_xor(g, off, 64);
+      if ((lane & 15) == 0) xgsum[(size_t)t * (d / 128) + (kk + 8 * lane) / 128] = g;
+    }
+  }
 }
 
 RouterSmallArgs router_small_args(const moe_config& c, const Plan& p, const uint16_t* hidden,
@@ -201,8 +217,10 @@ void launch_router(const moe_config& c, const Plan& p, const uint16_t* hidden, c
   else
     router_logits_mfma_kernel<16><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, E, kchunk, xperm,
                                                        xsum_part);
-  router_topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(logits, p.router_split, router_bias, p.T, E, k, ns, topk_idx,
-                                                   topk_w, xsum_part, reinterpret_cast<float*>(ws + p.xsum), flags);
+  router_topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(
+      logits, p.router_split, router_bias, p.T, E, k, ns, topk_idx, topk_w, xsum_part,
+      reinterpret_cast<float*>(ws + p.xsum), flags, hidden, c.d_model,
+      c.group_size && c.weight_bits == 4 ? reinterpret_cast<float*>(ws + p.xgsum) : nullptr);
 }
 
 }  // namespace moe
