@@ -49,10 +49,15 @@ __global__ __launch_bounds__(kPermuteThreads) void regroup_scatter_kernel(Regrou
   const int R = a.R, E = a.E, b = blockIdx.x;
   for (int e = tid; e < E; e += kPermuteThreads) {
     int t = 0, pre = 0;
-    for (int q = 0; q < nblocks; ++q) {
-      const int h = hist[(size_t)q * E + e];
-      if (q < b) pre += h;
-      t += h;
+    for (int q0 = 0; q0 < nblocks; q0 += 8) {  // eight loads in flight at a time
+      int h[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) h[u] = q0 + u < nblocks ? hist[(size_t)(q0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (q0 + u < b) pre += h[u];
+        t += h[u];
+      }
     }
     tot[e] = t;
     base[e] = pre;  // rows of e in earlier chunks; the group offset is added below
