@@ -17,6 +17,145 @@
 
 namespace moe {
 
+constexpr int kNoExpert = 0x7fffffff;
+
+// A lane's partner value in a DPP exchange inside its row of 16 lanes (CTRL:
+// a quad permutation or a row mirror, each an involution).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Max (NaN ignored) and min over an aligned segment of 2^LGS <= 16 lanes:
+// lane ^ 1, lane ^ 2, then the half-row and row mirrors; after the LGS steps
+// every lane of the segment holds the result.
+template <int LGS>
+__device__ __forceinline__ double segment_max(double v) {
+  if constexpr (LGS >= 1) v = fmax(v, dpp_f64<0xB1>(v));
+  if constexpr (LGS >= 2) v = fmax(v, dpp_f64<0x4E>(v));
+  if constexpr (LGS >= 3) v = fmax(v, dpp_f64<0x141>(v));
+  if constexpr (LGS >= 4) v = fmax(v, dpp_f64<0x140>(v));
+  return v;
+}
+template <int LGS>
+__device__ __forceinline__ int segment_min(int v) {
+  if constexpr (LGS >= 1) v = min(v, dpp_i32<0xB1>(v));
+  if constexpr (LGS >= 2) v = min(v, dpp_i32<0x4E>(v));
+  if constexpr (LGS >= 3) v = min(v, dpp_i32<0x141>(v));
+  if constexpr (LGS >= 4) v = min(v, dpp_i32<0x140>(v));
+  return v;
+}
+
+// Order of the segment top-k: a beats b if its logit is larger, or equal
+// with a lower id; a NaN logit (no expert, or one already chosen) beats
+// nothing and loses to everything else.
+__device__ __forceinline__ bool beats(double a, int ia, double b, int ib) {
+  return !__builtin_isnan(a) && (__builtin_isnan(b) || a > b || (a == b && ia < ib));
+}
+__device__ __forceinline__ void order_pair(double& a, int& ia, double& b, int& ib) {
+  const bool sw = beats(b, ib, a, ia);
+  const double x = a;
+  const int ix = ia;
+  a = sw ? b : a;
+  ia = sw ? ib : ia;
+  b = sw ? x : b;
+  ib = sw ? ix : ib;
+}
+
+// The k <= 8 rounds of the top-k of one token over a segment of 2^LGS lanes,
+// lane j holding experts j + 2^LGS m; lt: the token's E logits in LDS.  Every
+// lane of the segment ends with the chosen logits and ids in round order.
+//
+// At most four experts per lane: the lane sorts its four (logit, id) pairs
+// once, then each round reduces the heads of the segment's lanes (the largest
+// logit, then the lowest id holding it) and the winning lane pops its head.
+template <int LGS, int K8 = 8>
+__device__ __forceinline__ void topk_rounds_sorted(const double* lt, int E, int k, int j, double (&val)[K8],
+                                                   int (&cid)[K8]) {
+  double h[4];
+  int hid[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e2 = j + (m << LGS);
+    const double x = lt[min(e2, E - 1)];
+    h[m] = e2 < E ? x : __builtin_nan("");
+    hid[m] = e2 < E ? e2 : kNoExpert;
+  }
+  order_pair(h[0], hid[0], h[1], hid[1]);
+  order_pair(h[2], hid[2], h[3], hid[3]);
+  order_pair(h[0], hid[0], h[2], hid[2]);
+  order_pair(h[1], hid[1], h[3], hid[3]);
+  order_pair(h[1], hid[1], h[2], hid[2]);
+#pragma unroll
+  for (int r = 0; r < K8; ++r) {
+    val[r] = 0.0;
+    cid[r] = 0;
+    if (r < k) {
+      const double smx = segment_max<LGS>(h[0]);
+      const int win = segment_min<LGS>(h[0] == smx ? hid[0] : kNoExpert);
+      val[r] = smx;
+      cid[r] = win;
+      const bool pop = hid[0] == win;
+      h[0] = pop ? h[1] : h[0];
+      hid[0] = pop ? hid[1] : hid[0];
+      h[1] = pop ? h[2] : h[1];
+      hid[1] = pop ? hid[2] : hid[1];
+      h[2] = pop ? h[3] : h[2];
+      hid[2] = pop ? hid[3] : hid[2];
+      h[3] = pop ? __builtin_nan("") : h[3];
+      hid[3] = pop ? kNoExpert : hid[3];
+    }
+  }
+}
+
+// The same for more than four experts per lane: each round scans the lane's
+// logits in LDS (four loads in flight), reduces the segment, and retires the
+// winner by writing NaN over its logit (the LDS accesses of one wave take
+// effect in order, so the next round's reads see it).
+template <int LGS, int K8 = 8>
+__device__ __forceinline__ void topk_rounds_scan(double* lt, int E, int k, int j, double (&val)[K8],
+                                                 int (&cid)[K8]) {
+#pragma unroll
+  for (int r = 0; r < K8; ++r) {
+    val[r] = 0.0;
+    cid[r] = 0;
+    if (r < k) {
+      double mx = __builtin_nan("");
+      int id = kNoExpert;
+      for (int m0 = 0; j + (m0 << LGS) < E; m0 += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e2 = j + ((m0 + u) << LGS);
+          const double x = lt[min(e2, E - 1)];
+          const double v = e2 < E ? x : __builtin_nan("");
+          const bool take = beats(v, e2, mx, id);
+          mx = take ? v : mx;
+          id = take ? e2 : id;
+        }
+      }
+      const double smx = segment_max<LGS>(mx);
+      const int win = segment_min<LGS>(mx == smx ? id : kNoExpert);
+      val[r] = smx;
+      cid[r] = win;
+      if ((win & ((1 << LGS) - 1)) == j) lt[win] = __builtin_nan("");
+    }
+  }
+}
+
+template <int LGS>
+__device__ __forceinline__ void topk_rounds(double* lt, int E, int k, int j, double (&val)[8], int (&cid)[8]) {
+  if (E <= (4 << LGS))
+    topk_rounds_sorted<LGS>(lt, E, k, j, val, cid);
+  else
+    topk_rounds_scan<LGS>(lt, E, k, j, val, cid);
+}
+
 // Top-k of one token, run by one wave: add the bias to the (split-summed)
 // logits, then k rounds of a wave-wide arg-max over the experts not yet
 // chosen (largest logit, ties to the lower id), then
@@ -155,12 +294,15 @@ constexpr int router_small_lds_bytes() {
 // the end), k-split z of a.nsplit, one of `nblocks` blocks.  Its 4 waves take
 // a quarter of the split's k range each, lane l accumulating k = 8l .. 8l+7 of
 // every 512 for all tokens of the group, the loads of TG tokens in flight at
-// a time; a butterfly over the lanes and a fixed-order sum over the 4 waves
-// finish each partial logit.  The last block to finish (an atomic ticket)
+// a time; a reduce-scatter over the lanes and a fixed-order sum over the 4
+// waves finish each partial logit.  The last block to finish (an atomic ticket)
 // then runs the top-k of every token and the regroup, and clears the ticket
 // for the next call.  smem: router_small_lds_bytes<MAX_TE, MAX_T>() bytes,
-// 16-byte aligned.
-template <int MAX_TE, int MAX_T, int TG>
+// 16-byte aligned.  kWaveFinish = false leaves out the finish for T * E >
+// MAX_TE or T > MAX_T (one wave per token reading the logits from memory): its
+// caller's plan never runs such shapes, and that code would need scratch
+// memory beside a GEMM's register budget.
+template <int MAX_TE, int MAX_T, int TG, bool kWaveFinish = true>
 __device__ void router_small_body(const RouterSmallArgs& a, int e, int t0, int z, int nblocks, char* smem) {
   static_assert(kRouterTokTile % TG == 0, "token groups of the load loop");
   double (*part)[kRouterTokTile] = reinterpret_cast<double (*)[kRouterTokTile]>(smem);
@@ -201,15 +343,36 @@ __device__ void router_small_body(const RouterSmallArgs& a, int e, int t0, int z
       }
     }
   }
+  // Reduce-scatter over the lanes: at the exchanges with lane ^ 32, ^ 16, ^ 8
+  // and ^ 4 each lane keeps half of its tokens and adds its partner's half, so
+  // that a lane ends with one token, 8 b5 + 4 b4 + 2 b3 + b2 (b_i: bit i of
+  // the lane), summed over 16 lanes; lane ^ 2 and ^ 1 finish the sum.  Every
+  // logit of a token takes the same sequence of additions.
+  static_assert(kRouterTokTile == 16, "four halving exchanges");
+  double r8[8], r4[4], r2[2], r1;
+  {
+    const bool hi = lane & 32;
 #pragma unroll
-  for (int t = 0; t < kRouterTokTile; ++t) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc[t] += __shfl_xor(acc[t], off, 64);
+    for (int i = 0; i < 8; ++i) r8[i] = (hi ? acc[8 + i] : acc[i]) + __shfl_xor(hi ? acc[i] : acc[8 + i], 32, 64);
   }
-  if (lane == 0) {
+  {
+    const bool hi = lane & 16;
 #pragma unroll
-    for (int t = 0; t < kRouterTokTile; ++t) part[wave][t] = acc[t];
+    for (int i = 0; i < 4; ++i) r4[i] = (hi ? r8[4 + i] : r8[i]) + __shfl_xor(hi ? r8[i] : r8[4 + i], 16, 64);
   }
+  {
+    const bool hi = lane & 8;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r2[i] = (hi ? r4[2 + i] : r4[i]) + __shfl_xor(hi ? r4[i] : r4[2 + i], 8, 64);
+  }
+  {
+    const bool hi = lane & 4;
+    r1 = (hi ? r2[1] : r2[0]) + __shfl_xor(hi ? r2[0] : r2[1], 4, 64);
+  }
+  r1 += __shfl_xor(r1, 2, 64);
+  r1 += __shfl_xor(r1, 1, 64);
+  if ((lane & 3) == 0)
+    part[wave][((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1)] = r1;
   __syncthreads();
   if (wave == 0 && lane < nt) {
     const double v = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
@@ -260,65 +423,50 @@ __device__ void router_small_body(const RouterSmallArgs& a, int e, int t0, int z
       }
     }
     __syncthreads();
-    // Top-k of every token at once: a segment of S lanes per token (S a power
-    // of two, S * T <= 256), lane j of the segment holding experts j, j + S,
-    // ...  Each of the k rounds takes every lane's best live expert (largest
-    // fp64 logit, lowest id), reduces the segment with a butterfly, and
-    // retires the winner; w_j = exp(l_j - l_0) / sum exp(l_i - l_0).
-    int S = 64;
-    while (S > 1 && S * T > 256) S >>= 1;
-    const int seg = threadIdx.x / S, j = threadIdx.x % S;
-    const int t = seg;
-    if (t < T) {
-      const double* lt = lg + (size_t)t * E;
-      uint64_t dead = 0;  // bit m: expert j + S m chosen (E / S <= 64)
+    // Top-k of every token at once: a segment of S = 2^lgS lanes per token
+    // (S <= 16, S * T <= 256), lane j of the segment holding experts j,
+    // j + S, ...; k rounds each take the largest live logit of the segment (a
+    // max reduction with DPP exchanges inside the lane's row of 16), then the
+    // lowest id holding it (a min reduction), and retire that expert
+    // (topk_rounds).  NaN marks "no expert" (fmax ignores it, and it equals
+    // nothing; the logits of finite inputs are finite).  This code runs on one
+    // block while the rest of the GPU waits, so it is written for a short
+    // dependent chain per round rather than for throughput.
+    // w_j = exp(l_j - l_0) / sum exp(l_i - l_0).
+    int lgS = 4;
+    while (lgS > 0 && (T << lgS) > 256) --lgS;
+    const int S = 1 << lgS;
+    const int t = threadIdx.x >> lgS, j = threadIdx.x & (S - 1);
+    if (t < T) {  // segments are aligned, so a segment is wholly inside or outside
+      double* lt = lg + (size_t)t * E;
       double val[8];
       int cid[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        val[r] = 0.0;
-        cid[r] = 0;
-        if (r < k) {
-          double best = 0.0;
-          int bid = 0x7fffffff;
-          for (int e2 = j, m = 0; e2 < E; e2 += S, ++m) {
-            const double v = lt[e2];
-            if (!((dead >> m) & 1) && (bid == 0x7fffffff || v > best)) {
-              best = v;
-              bid = e2;
-            }
-          }
-          for (int off = S >> 1; off >= 1; off >>= 1) {
-            const double ov = __shfl_xor(best, off, 64);
-            const int oid = __shfl_xor(bid, off, 64);
-            if (oid != 0x7fffffff && (bid == 0x7fffffff || ov > best || (ov == best && oid < bid))) {
-              best = ov;
-              bid = oid;
-            }
-          }
-          val[r] = best;
-          cid[r] = bid;
-          if (bid % S == j) dead |= 1ull << (bid / S);
-        }
+      switch (lgS) {
+        case 4: topk_rounds<4>(lt, E, k, j, val, cid); break;
+        case 3: topk_rounds<3>(lt, E, k, j, val, cid); break;
+        case 2: topk_rounds<2>(lt, E, k, j, val, cid); break;
+        case 1: topk_rounds<1>(lt, E, k, j, val, cid); break;
+        default: topk_rounds<0>(lt, E, k, j, val, cid); break;
       }
       if (j == 0) {
+        // (the hardware exp2 of an fp32 argument <= 0 and one reciprocal:
+        // errors near 1e-7, far inside what fp32 weights carry anyway)
         float ex[8], den = 0.0f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          ex[r] = r < k ? expf((float)(val[r] - val[0])) : 0.0f;
+          ex[r] = r < k ? __expf((float)(val[r] - val[0])) : 0.0f;
           den += ex[r];
         }
+        const float inv = 1.0f / den;
         const int kt = k + ns;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          if (r < k) {
-            a.topk_idx[(size_t)t * kt + r] = cid[r];
-            a.topk_w[(size_t)t * kt + r] = ex[r] / den;
-            sid[t * kt + r] = cid[r];
-          } else if (r < kt) {  // shared experts
-            a.topk_idx[(size_t)t * kt + r] = E + r - k;
-            a.topk_w[(size_t)t * kt + r] = 1.0f;
-            sid[t * kt + r] = E + r - k;
+          if (r < kt) {
+            const bool routed = r < k;
+            const int e2 = routed ? cid[r] : E + r - k;  // then the shared experts
+            a.topk_idx[(size_t)t * kt + r] = e2;
+            a.topk_w[(size_t)t * kt + r] = routed ? ex[r] * inv : 1.0f;
+            sid[t * kt + r] = e2;
           }
         }
       }
@@ -327,7 +475,8 @@ __device__ void router_small_body(const RouterSmallArgs& a, int e, int t0, int z
     if (a.tmask && T <= 31) {
       for (int x = threadIdx.x; x < ra.E; x += 256) {
         uint32_t m = 0;
-        for (int i = 0; i < T * (k + ns); ++i) m |= (sid[i] == x ? 1u : 0u) << (i / (k + ns));
+        for (int tt = 0, i = 0; tt < T; ++tt)
+          for (int r = 0; r < k + ns; ++r, ++i) m |= (sid[i] == x ? 1u : 0u) << tt;
         __hip_atomic_store(&a.tmask[x], m | kMaskKnown, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -338,10 +487,12 @@ __device__ void router_small_body(const RouterSmallArgs& a, int e, int t0, int z
     if (threadIdx.x == 0) reset_ticket(a.ticket);
     return;
   }
-  for (int t = wave; t < T; t += 4)
-    topk_token<true>(a.logits, nsplit, a.bias, T, E, k, ns, t, lane, a.topk_idx, a.topk_w);
-  __syncthreads();
-  regroup_block<256>(ra, rg_lds);
+  if constexpr (kWaveFinish) {
+    for (int t = wave; t < T; t += 4)
+      topk_token<true>(a.logits, nsplit, a.bias, T, E, k, ns, t, lane, a.topk_idx, a.topk_w);
+    __syncthreads();
+    regroup_block<256>(ra, rg_lds);
+  }
   if (threadIdx.x == 0) reset_ticket(a.ticket);
 }
 

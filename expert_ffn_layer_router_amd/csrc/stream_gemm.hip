@@ -636,7 +636,7 @@ void stream_gemm_router_kernel(StreamArgs a, RouterSmallArgs r, int nrouter) {
   __shared__ __attribute__((aligned(1024))) char smem[kGemm > kRouter ? kGemm : kRouter];
   const int b = blockIdx.x;
   if (b < nrouter) {
-    router_small_body<kDenseRouterLogits, kRouterTokTile, 8>(r, b % r.E, 0, b / r.E, nrouter, smem);
+    router_small_body<kDenseRouterLogits, kRouterTokTile, 8, false>(r, b % r.E, 0, b / r.E, nrouter, smem);
     return;
   }
   const int g = b - nrouter, ncb = a.dff / (64 * NCW);

@@ -112,6 +112,31 @@ def test_small_special_shapes(E, k, S):
         assert np.all(np.sort(res["topk_idx"], axis=1) == np.arange(E + S))
 
 
+@pytest.mark.parametrize("T,E,k,zero", [(16, 128, 8, False), (16, 128, 8, True), (8, 256, 3, False),
+                                         (32, 40, 5, False), (20, 32, 2, False), (20, 32, 4, True),
+                                         (64, 64, 6, False), (1, 64, 8, False)])
+def test_few_token_topk_shapes(T, E, k, zero):
+    """The few-token router's finish at every segment width it uses (16 lanes
+    per token up to T = 16, 8 up to 32, 4 up to 64) and both of its round
+    forms (at most four experts per lane held sorted in registers, more read
+    from LDS each round); `zero`: a zero router, every logit tied."""
+    require_gpu()
+    shape = synth.LayerShape(T, 128, 256, E, k, E, "identity", 1.0)
+    w = synth.make_weights(shape, seed=5)
+    x = synth.make_hidden(T, 128, seed=5)
+    case = synth.Case("topk", shape, 5, x, w)
+    over = {}
+    if zero:
+        over = dict(router_w=np.zeros((E, 128), np.float32), router_b=np.zeros(E, np.float32))
+    say(f"few-token top-k T={T} E={E} k={k} zero={zero}")
+    res = GpuLayer(shape, w, max_tokens=T).run(x, **over)
+    ref = _oracle(case, **over)
+    check_routing(res, ref)
+    if zero:
+        assert np.all(res["topk_idx"] == np.arange(k)[None, :])
+    assert_out_close(res["out"], ref["out"])
+
+
 @pytest.mark.parametrize("T", [16, 300])
 def test_out_of_range_slot_sets_flag_and_contributes_zero(T):
     require_gpu()
