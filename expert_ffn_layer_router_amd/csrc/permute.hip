@@ -4,14 +4,13 @@
 // so that each expert's tokens are contiguous and its weights are loaded once
 // for all of them; section 3.2 runs the group GEMM over these groups.
 //
-// One workgroup: an LDS histogram of the expert ids, an exclusive scan, then
-// a stable counting-sort scatter.  Rows keep ascending assignment order
-// a = t*k + j inside each expert's group: NT assignments are placed per
-// round; inside a wave a lane's rank among same-expert lanes comes from
-// ballots over the bits of the id, and across waves from per-wave counts in
-// LDS.  Also emits the GEMM row-tile list: one descriptor (expert, slot,
-// first grouped row, rows) for every tile_rows rows of every non-empty group,
-// in expert order.
+// One workgroup: per-wave expert counts, an exclusive scan, then a stable
+// counting-sort scatter.  Rows keep ascending assignment order a = t*k + j
+// inside each expert's group: inside a wave a lane's rank among same-expert
+// lanes comes from ballots over the bits of the id, and across waves from the
+// per-wave counts in LDS.  Also emits the GEMM row-tile list: one descriptor
+// (expert, slot, first grouped row, rows) for every tile_rows rows of every
+// non-empty group, in expert order.
 #include "device_common.h"
 #include "plan.h"
 #include "regroup.h"
@@ -19,8 +18,12 @@
 namespace moe {
 
 __global__ __launch_bounds__(kPermuteThreads) void permute_kernel(RegroupArgs a) {
+  // R <= kPermuteThreads: the one-pass form
   __shared__ __attribute__((aligned(16))) char lds[regroup_lds_bytes<kPermuteThreads>()];
-  regroup_block<kPermuteThreads>(a, lds);
+  for (int x = threadIdx.x; x < (kPermuteThreads / 64) * 256; x += kPermuteThreads)
+    regroup_wave_counts<kPermuteThreads>(lds)[x] = 0;
+  __syncthreads();
+  regroup_block_onepass<kPermuteThreads>(a, lds);
 }
 
 // Many rows: the same regroup over chunks of kPermuteThreads assignments, one

@@ -125,4 +125,98 @@ __device__ void regroup_block(const RegroupArgs& a, char* lds) {
   }
 }
 
+// The same regroup in one pass for R <= NT rows (one row per thread), with
+// fewer barriers: the ballot ranks give every wave's count per expert at
+// once, so no LDS histogram is needed.  The caller has zeroed the per-wave
+// counts, regroup_wave_counts(lds), and passed a barrier since.  Same outputs,
+// bit for bit, as regroup_block.
+template <int NT>
+__device__ __forceinline__ int* regroup_wave_counts(char* lds) {
+  return reinterpret_cast<int*>(lds);  // [NT / 64][256]
+}
+template <int NT>
+__device__ void regroup_block_onepass(const RegroupArgs& a, char* lds) {
+  constexpr int NW = NT / 64;
+  static_assert(NT >= 256, "one thread per expert in the scan");
+  int (*wc)[256] = reinterpret_cast<int (*)[256]>(regroup_wave_counts<NT>(lds));
+  int* wtot = reinterpret_cast<int*>(lds + NW * 256 * 4);  // [2][4]: the scan's wave totals
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int R = a.R, E = a.E, tr = a.tile_rows;
+  // this row's expert, its rank among the wave's rows of that expert, and
+  // (by the first of them) the wave's count of that expert
+  const bool valid = tid < R;
+  const int e = valid ? a.topk_idx[tid] : 0;
+  uint64_t peers = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(peers & lt_mask);
+  if (valid && rank == 0) wc[wave][e] = __popcll(peers);
+  __syncthreads();
+  // thread x < 256: expert x's rows and row tiles, exclusive scans of both
+  // over the experts (lane scans, then the totals of the waves before)
+  int c = 0, nt = 0, ic = 0, it = 0;
+  if (tid < 256) {
+    if (tid < E) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) c += wc[w][tid];
+      nt = (c + tr - 1) / tr;
+    }
+    ic = c;
+    it = nt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int uc = __shfl_up(ic, off, 64), ut = __shfl_up(it, off, 64);
+      if (lane >= off) {
+        ic += uc;
+        it += ut;
+      }
+    }
+    if (lane == 63) {
+      wtot[wave] = ic;
+      wtot[4 + wave] = it;
+    }
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int bc = 0, bt = 0;
+    for (int w = 0; w < wave; ++w) {
+      bc += wtot[w];
+      bt += wtot[4 + w];
+    }
+    const int base = bc + ic - c;
+    if (tid < E) {
+      a.offsets[tid] = base;
+      a.counts[tid] = c;
+      // the waves' first positions in the group, in place of their counts
+      int run = base;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int v = wc[w][tid];
+        wc[w][tid] = run;
+        run += v;
+      }
+      if (c > 0) {
+        const int slot = a.slot_table[tid];
+        int ti = bt + it - nt;
+        for (int r0 = 0; r0 < c; r0 += tr) a.tiles[ti++] = make_int4(tid, slot, base + r0, min(tr, c - r0));
+      }
+    }
+    if (tid == 255) {
+      a.offsets[E] = bc + ic;
+      *a.num_tiles = bt + it;
+    }
+  }
+  __syncthreads();
+  if (valid) {
+    const int pos = wc[wave][e] + rank;
+    a.perm[pos] = tid;
+    a.inv[tid] = pos;
+  }
+}
+
 }  // namespace moe

@@ -471,6 +471,10 @@ __device__ void router_small_body(const RouterSmallArgs& a, int e, int t0, int z
         }
       }
     }
+    // few rows: the one-pass regroup, whose per-wave counts start at zero
+    const bool onepass = ra.R <= 256;
+    if (onepass)
+      for (int x = threadIdx.x; x < 4 * 256; x += 256) regroup_wave_counts<256>(rg_lds)[x] = 0;
     __syncthreads();
     if (a.tmask && T <= 31) {
       for (int x = threadIdx.x; x < ra.E; x += 256) {
@@ -483,7 +487,10 @@ __device__ void router_small_body(const RouterSmallArgs& a, int e, int t0, int z
     RegroupArgs la = ra;
     la.topk_idx = sid;
     la.slot_table = sslot;
-    regroup_block<256>(la, rg_lds);
+    if (onepass)
+      regroup_block_onepass<256>(la, rg_lds);
+    else
+      regroup_block<256>(la, rg_lds);
     if (threadIdx.x == 0) reset_ticket(a.ticket);
     return;
   }
