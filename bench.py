@@ -48,6 +48,7 @@ DECODE_BOUND = {"mixtral_decode": "hbm", "phi35_skew": "hbm", "fine_decode": "hb
                 "mixtral_prefill_q4g128": "mfma", "mixtral_prefill_q8g128": "mfma"}
 CSRC = os.path.join(ROOT, "expert_ffn_layer_router_amd", "csrc")
 STREAM_MAX_TOKENS = 64   # the library's decode (weight-streaming) family runs up to this T
+FUSED_COMBINE_MAX_T = 8  # up to this T its down kernel's last blocks also run the combine
 
 
 def dense_decode(shape) -> bool:
@@ -327,7 +328,11 @@ def build_layer_graph(layers, pools, outs, x, rw, rb, st, ws, stream, torch):
     with its own handle, weight pool pools[i % len(pools)] and output outs[i],
     all reading the same hidden state and sharing one workspace -- a model's
     decode-step graph, each layer with its own weights.  The handles run once
-    eagerly first (outside the capture)."""
+    eagerly first (outside the capture), after the work already queued on the
+    current stream (the workspace's zero fill, pool copies): the library needs
+    the workspace's control words at zero before its first use."""
+    stream.wait_stream(torch.cuda.current_stream())
+
     def run_all():
         for i, L in enumerate(layers):
             L.forward(x, rw, rb, st, pools[i % len(pools)], out=outs[i], workspace=ws, stream=stream)
@@ -455,10 +460,13 @@ def run_workload(name, steps, warmup, torch, *, mode="layers", model_layers=32, 
             for key, v in ms.items():
                 stage_sum[key] = stage_sum.get(key, 0.0) + v
             L.set_stage_timing(0)
-        # few tokens: the regroup runs inside the router kernel and the combine
-        # inside the down kernel -- no kernel of their own to time; dense tiles:
-        # the router runs inside the gate/up launch
-        fused = ("regroup", "combine") if plan_fused else ()
+        # few tokens: the regroup runs inside the router kernel (and up to
+        # FUSED_COMBINE_MAX_T tokens the combine inside the down kernel) -- no
+        # kernel of their own to time; dense tiles: the router runs inside the
+        # gate/up launch
+        fused = ("regroup",) if plan_fused else ()
+        if T <= FUSED_COMBINE_MAX_T:
+            fused += ("combine",)
         if dense:
             fused += ("router",)
         stage_us = {key: 1e3 * v / max(1, n_fw) for key, v in stage_sum.items() if key not in fused}

@@ -56,6 +56,49 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   *reinterpret_cast<u32x4*>(out + (size_t)t * d + c) = o;
 }
 
+// Few tokens, the down kernel's fp32 partials ypart[split][p][d]: per output
+// the rows j = 0..k-1 in order, each the sum of its splits in split order,
+// weighted -- the same operations, in the same order, as the combine the down
+// kernel runs in its last blocks.  One thread: 4 columns of one token.
+__global__ __launch_bounds__(256) void combine_partials_kernel(const float* __restrict__ ypart, int R, int d,
+                                                               int nsplit, const int32_t* __restrict__ inv,
+                                                               const float* __restrict__ topk_w, int T, int k,
+                                                               uint16_t* __restrict__ out) {
+  const int per_row = d / 4;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * per_row) return;
+  const int t = idx / per_row, c = (idx % per_row) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int p = inv[t * k + j];
+    const float w = topk_w[t * k + j];
+    float4 v = *reinterpret_cast<const float4*>(ypart + (size_t)p * d + c);
+    for (int sp = 1; sp < nsplit; ++sp) {
+      const float4 u = *reinterpret_cast<const float4*>(ypart + ((size_t)sp * R + p) * d + c);
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+  }
+  uint2 o;
+  o.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
+  o.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+  *reinterpret_cast<uint2*>(out + (size_t)t * d + c) = o;
+}
+
+void launch_combine_partials(const moe_config& c, const Plan& p, uint16_t* out, char* ws, hipStream_t s) {
+  const int n = p.T * (c.d_model / 4);
+  combine_partials_kernel<<<(n + 255) / 256, 256, 0, s>>>(
+      reinterpret_cast<const float*>(ws + p.y), p.R, c.d_model, p.down_split,
+      reinterpret_cast<const int32_t*>(ws + p.inv), reinterpret_cast<const float*>(ws + p.topk_w), p.T, c.top_k,
+      out);
+}
+
 void launch_combine(const moe_config& c, const Plan& p, uint16_t* out, char* ws, hipStream_t s) {
   const size_t n = (size_t)p.T * (c.d_model / 8);
   combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(

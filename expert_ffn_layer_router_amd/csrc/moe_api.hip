@@ -105,6 +105,13 @@ bool api_check_handle(moe_handle h, const moe_config** cfg) {
 #ifndef MOE_DENSE_IDLE_MAX
 #define MOE_DENSE_IDLE_MAX 0.02  // dense tiles while an expert without routed rows is at most this likely
 #endif
+#ifndef MOE_FUSED_COMBINE_MAX_T
+// Up to this T the down kernel's last blocks run the combine; above it a
+// kernel of its own (after a launch gap) beats them: the last block of a
+// column slice gathers T x 64 outputs through coherent loads, one round trip
+// past the L2 each (T = 64 layer steps: 178 -> 166 us Mixtral-shaped).
+#define MOE_FUSED_COMBINE_MAX_T 8
+#endif
 
 namespace moe {
 
@@ -125,6 +132,7 @@ void make_plan(const moe_config& c, int T, Plan* p) {
     p->tile_rows = kPrefillTileRows;
   }
   p->fused_small = T <= kStreamMaxTokens;
+  p->fused_combine = p->fused_small && T <= MOE_FUSED_COMBINE_MAX_T;
   if (T <= kStreamMaxTokens) {
     p->router_split = 0;
     // one 512-k pass per wave: k-split in multiples of 128, up to kRouterSmallMaxSplit
@@ -279,7 +287,10 @@ moe_status enqueue(moe_layer* h, const moe::Plan& p, const uint16_t* hidden, con
   mark(3);
   moe::launch_down(c, p, slot_table, *w, out, ws, s);
   mark(4);
-  if (!p.fused_small) moe::launch_combine(c, p, out, ws, s);
+  if (!p.fused_small)
+    moe::launch_combine(c, p, out, ws, s);
+  else if (!p.fused_combine)
+    moe::launch_combine_partials(c, p, out, ws, s);
   mark(5);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));

@@ -54,7 +54,11 @@ struct Plan {
   int tile_rows = kPrefillTileRows;  // rows of an expert group per GEMM row tile
   int down_split = 1;         // k-split of the down projection
   int max_tiles = 0;          // upper bound on GEMM row tiles
-  bool fused_small = false;   // few tokens: router + top-k + regroup in one kernel, combine fused into down
+  bool fused_small = false;   // few tokens: router + top-k + regroup in one kernel
+  // few tokens: the combine runs in the down kernel (the last block of each
+  // column slice); otherwise, with fused_small, a kernel of its own sums the
+  // down kernel's fp32 partials
+  bool fused_combine = false;
   // few tokens and nearly every expert routed to: dense tiles (every expert
   // with all T tokens), the router launched beside the gate/up GEMM
   bool dense = false;
@@ -96,5 +100,7 @@ void launch_gateup_prefill(const moe_config& c, const Plan& p, const uint16_t* h
                            char* ws, hipStream_t s);
 void launch_down_prefill(const moe_config& c, const Plan& p, const moe_weights& w, char* ws, hipStream_t s);
 void launch_combine(const moe_config& c, const Plan& p, uint16_t* out, char* ws, hipStream_t s);
+// fused_small without fused_combine: out from the down kernel's fp32 partials
+void launch_combine_partials(const moe_config& c, const Plan& p, uint16_t* out, char* ws, hipStream_t s);
 
 }  // namespace moe

@@ -29,10 +29,11 @@
 // which is linear in the k parts, and the parts are added in a fixed order
 // through LDS by the wave that owns each column tile, which also stores it.
 //
-// With few tokens the weighted scatter-back (combine) is fused into the down
-// kernel: the last block to finish a 64-column slice (an atomic ticket per
-// slice in the workspace's control words) sums that slice of every token's
-// expert rows, in the same fixed order as the stand-alone combine kernel.
+// With very few tokens the weighted scatter-back (combine) is fused into the
+// down kernel: the last block to finish a 64-column slice (an atomic ticket
+// per slice in the workspace's control words) sums that slice of every
+// token's expert rows, in the same fixed order as the stand-alone kernel that
+// otherwise sums the partials after it (combine.hip).
 #include "device_common.h"
 #include "plan.h"
 #include "router_small.h"
@@ -156,6 +157,16 @@ struct StreamArgs {
   uint32_t* tmask;            // [E] dense plans: the router's token masks (control words)
 };
 
+// The down kernel's partial outputs: read by its own last blocks (fused
+// combine: coherent stores, the readers are other blocks of this kernel) or
+// by the next kernel (plain stores: the kernel boundary orders them).
+__device__ __forceinline__ void store_y(const StreamArgs& a, float* p, float v) {
+  if (a.fc.tickets)
+    store_coherent(p, v);
+  else
+    *p = v;
+}
+
 // Fused combine: the last block to finish a column slice (an atomic ticket
 // per slice) gathers that slice of out[] for every token: per token the k
 // routed rows in order j = 0..k-1, each the fixed-order sum of its k-splits.
@@ -271,7 +282,7 @@ __device__ __forceinline__ void stream_gemm_body(const StreamArgs& a, int bx, in
   if (bad) {
     if (threadIdx.x == 0 && !dense_tile) atomicOr(a.flags, MOE_FLAG_BAD_SLOT);
     if (GATEUP) return;
-    for (int i = threadIdx.x; i < rows * COLS; i += 256) store_coherent(&yrow[(size_t)(i / COLS) * a.d + n0 + i % COLS], 0.0f);
+    for (int i = threadIdx.x; i < rows * COLS; i += 256) store_y(a, &yrow[(size_t)(i / COLS) * a.d + n0 + i % COLS], 0.0f);
   } else {
     // this lane's activation rows (row lr + 16 g of the tile) and k offset in
     // every stage: KR kp + (KR / 4) grp, KS x 8 values
@@ -591,7 +602,7 @@ __device__ __forceinline__ void stream_gemm_body(const StreamArgs& a, int bx, in
             if (GATEUP)
               hrow[(uint32_t)(row * a.dff + h_phys_col(nl))] = f32_to_bf16(silu(v0[i]) * v1[i]);
             else
-              store_coherent(&ybase[(uint32_t)(row * a.d + nl)], v0[i]);
+              store_y(a, &ybase[(uint32_t)(row * a.d + nl)], v0[i]);
           }
         }
       }
@@ -757,7 +768,7 @@ void launch_down_stream(const moe_config& c, const Plan& p, const int32_t* slot_
   a.s0 = w.s_down;
   a.z0 = w.z_down;
   a.ypart = reinterpret_cast<float*>(ws + p.y);
-  if (p.fused_small) {
+  if (p.fused_combine) {
     a.fc.tickets = reinterpret_cast<uint32_t*>(ws + p.ctrl) + 1;
     a.fc.inv = reinterpret_cast<const int32_t*>(ws + p.inv);
     a.fc.topk_w = reinterpret_cast<const float*>(ws + p.topk_w);

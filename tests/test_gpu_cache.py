@@ -33,6 +33,7 @@ def test_refill_from_host_on_a_copy_stream_matches_the_oracle(bits, group):
                  weight_bits=bits, group_size=group)
     ws = g.new_workspace(T)
     out = torch.empty((T, shape.d_model), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()  # the zero fill and the pool upload run on the default stream
     compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
     rws = [to_device(w.router_w) for w in layers]
     table = [cache.request(i, [])[2] for i in range(L)]

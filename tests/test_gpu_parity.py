@@ -231,6 +231,7 @@ def test_graph_replay_matches_eager_and_reads_inputs_at_replay(name):
     table = gl.to_device(w.slot_table)
     out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
     ws = gl.layer.new_workspace(T)
+    torch.cuda.synchronize()  # the zero fill runs on the default stream, the replays on `stream`
     say(f"{name}: capture, T={T}")
     with torch.cuda.stream(stream):
         gl.layer.capture(xb, gl.router_w, gl.router_b, table, gl.dw, out, ws, stream)
@@ -387,7 +388,7 @@ def test_layers_graph_at_the_benchmarked_decode_shape_matches_the_oracle():
     layers = [MoeLayer(d, shape.d_ff, shape.num_experts, shape.top_k, shape.num_slots, T) for _ in range(nl)]
     outs = [torch.empty((T, d), dtype=torch.bfloat16, device="cuda") for _ in range(nl)]
     ws = layers[0].new_workspace(T)
-    stream = torch.cuda.Stream()
+    stream = torch.cuda.Stream()  # (build_layer_graph orders it after the zero fill and pool copies)
     graph = bench.build_layer_graph(layers, pools, outs, x, rw, None, st, ws, stream, torch)
     ref = _oracle(case)
     for rep in range(3):
