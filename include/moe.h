@@ -38,9 +38,12 @@
  *   - Device pointers are caller-owned, must be 16-byte aligned, and must stay
  *     valid until the enqueued work completes.  The library allocates no
  *     device memory; all intermediates live in the caller's workspace.
- *   - A workspace must be zero-filled once before its first use.  Its first
- *     bytes hold control words (completion tickets of fused kernels) that
- *     every call leaves zero again, so later calls need no clearing.
+ *   - A workspace must be zero-filled once before its first use, and the
+ *     fill must be complete, or ordered on `stream`, when that first call's
+ *     work starts (a fill on another stream needs an event or a
+ *     synchronisation).  Its first bytes hold control words (completion
+ *     tickets of fused kernels) that every call leaves zero again, so later
+ *     calls need no clearing.
  *   - moe_forward and moe_graph_launch only enqueue work on `stream` (a
  *     hipStream_t; NULL means the null stream): no host synchronisation.
  *   - Calls that share one workspace must not overlap in time.
