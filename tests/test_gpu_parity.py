@@ -70,7 +70,10 @@ def test_layer_parity(name):
                                     ("shared_tiny", 33), ("shared_tiny", 300), ("fine_shared_tiny", 64),
                                     ("fine_shared_tiny", 65), ("tiny_q4g128", 1), ("tiny_q4g128", 33),
                                     ("tiny_q4g128", 65), ("tiny_q4g128", 300), ("tiny_q8", 40), ("tiny_q8", 200),
-                                    ("tiny_q8g128", 17), ("tiny_q8g128", 129)])
+                                    ("tiny_q8g128", 17), ("tiny_q8g128", 129),
+                                    # Mixtral-shaped routed decode: the combine in the down kernel (T <= 8)
+                                    # and in a kernel of its own (32-row tiles)
+                                    ("mixtral_decode", 8), ("mixtral_decode", 40)])
 def test_ragged_token_counts(name, T):
     require_gpu()
     case = synth.make_case(name, T=T)
