@@ -166,6 +166,96 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const double* __restri
   }
 }
 
+// The same for at most 64 routed experts with 16 lanes per token (four
+// tokens per wave): lane j holds experts j, j + 16, j + 32, j + 48, each
+// logit the same sum (splits in order, then the bias), chosen by the rounds
+// of topk_rounds_heads (one max and one min reduction per round, DPP
+// exchanges inside the segment) instead of k rounds of a 64-lane butterfly.
+// The weights, the row sum and the group sums take the same operations as in
+// router_topk_kernel (the row sum's parts in another fixed order).
+__global__ __launch_bounds__(256) void router_topk_seg_kernel(const double* __restrict__ logits, int nsplit,
+                                                              const float* __restrict__ bias, int T, int E, int k,
+                                                              int ns, int32_t* __restrict__ topk_idx,
+                                                              float* __restrict__ topk_w,
+                                                              const double* __restrict__ xsum_part,
+                                                              float* __restrict__ xsum, uint32_t* __restrict__ flags,
+                                                              const uint16_t* __restrict__ hidden, int d,
+                                                              float* __restrict__ xgsum) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (t >= T) return;  // whole segments: the exchanges below stay inside one
+  const int j = threadIdx.x & 15;
+  // the row sum's parts first (lane j: splits j, j + 16, ...)
+  double sx = 0.0;
+  for (int s = j; s < nsplit; s += 16) sx += xsum_part[(size_t)s * T + t];
+  double h[4];
+  int hid[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = j + 16 * m;
+    const bool ok = e < E;
+    const int ee = ok ? e : 0;
+    double v = 0.0;
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {  // eight loads in flight (a missing split adds +0.0)
+      double q[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) q[u] = s0 + u < nsplit ? logits[((size_t)(s0 + u) * T + t) * E + ee] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v += q[u];
+    }
+    if (bias) v += (double)bias[ee];
+    h[m] = ok ? v : __builtin_nan("");
+    hid[m] = ok ? e : kNoExpert;
+  }
+  double val[8];
+  int cid[8];
+  topk_rounds_heads<4>(h, hid, k, val, cid);
+  // lane j < k takes choice j: exp(l_j - l_0), then the sum in order j = 0 .. k-1
+  double bj = val[0];
+  int ij = cid[0];
+#pragma unroll
+  for (int r = 1; r < 8; ++r)
+    if (j == r) {
+      bj = val[r];
+      ij = cid[r];
+    }
+  const double ex = j < k ? exp(bj - val[0]) : 0.0;
+  double den = 0.0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const double er = __shfl(ex, r, 16);
+    if (r < k) den += er;
+  }
+  const int kt = k + ns;
+  if (j < k) {
+    topk_idx[(size_t)t * kt + j] = ij;
+    topk_w[(size_t)t * kt + j] = (float)(ex / den);
+  }
+  if (j == 0) {
+    for (int q = 0; q < ns; ++q) {
+      topk_idx[(size_t)t * kt + k + q] = E + q;
+      topk_w[(size_t)t * kt + k + q] = 1.0f;
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) sx += __shfl_xor(sx, off, 16);
+  if (j == 0) xsum[t] = (float)sx;
+  if (xgsum) {
+    // one group of 128 k at a time: lane j sums k = 8 j .. 8 j + 7 of it, then
+    // a butterfly over the segment
+    for (int g = 0; g < d / 128; ++g) {
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(hidden + (size_t)t * d + 128 * g + 8 * j);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      float gs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gs += __uint_as_float(xw[i] << 16) + __uint_as_float(xw[i] & 0xFFFF0000u);
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) gs += __shfl_xor(gs, off, 16);
+      if (j == 0) xgsum[(size_t)t * (d / 128) + g] = gs;
+    }
+  }
+}
+
 RouterSmallArgs router_small_args(const moe_config& c, const Plan& p, const uint16_t* hidden,
                                   const float* router_w, const float* router_bias, const int32_t* slot_table,
                                   char* ws) {
@@ -217,10 +307,16 @@ void launch_router(const moe_config& c, const Plan& p, const uint16_t* hidden, c
   else
     router_logits_mfma_kernel<16><<<grid, 256, 0, s>>>(hidden, router_w, logits, p.T, c.d_model, E, kchunk, xperm,
                                                        xsum_part);
-  router_topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(
-      logits, p.router_split, router_bias, p.T, E, k, ns, topk_idx, topk_w, xsum_part,
-      reinterpret_cast<float*>(ws + p.xsum), flags, hidden, c.d_model,
-      c.group_size && c.weight_bits == 4 ? reinterpret_cast<float*>(ws + p.xgsum) : nullptr);
+  float* xgsum = c.group_size && c.weight_bits == 4 ? reinterpret_cast<float*>(ws + p.xgsum) : nullptr;
+  if (E <= 64)
+    router_topk_seg_kernel<<<(p.T + 15) / 16, 256, 0, s>>>(logits, p.router_split, router_bias, p.T, E, k, ns,
+                                                           topk_idx, topk_w, xsum_part,
+                                                           reinterpret_cast<float*>(ws + p.xsum), flags, hidden,
+                                                           c.d_model, xgsum);
+  else
+    router_topk_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(logits, p.router_split, router_bias, p.T, E, k, ns, topk_idx,
+                                                     topk_w, xsum_part, reinterpret_cast<float*>(ws + p.xsum), flags,
+                                                     hidden, c.d_model, xgsum);
 }
 
 }  // namespace moe

@@ -69,24 +69,15 @@ __device__ __forceinline__ void order_pair(double& a, int& ia, double& b, int& i
 }
 
 // The k <= 8 rounds of the top-k of one token over a segment of 2^LGS lanes,
-// lane j holding experts j + 2^LGS m; lt: the token's E logits in LDS.  Every
-// lane of the segment ends with the chosen logits and ids in round order.
-//
-// At most four experts per lane: the lane sorts its four (logit, id) pairs
-// once, then each round reduces the heads of the segment's lanes (the largest
-// logit, then the lowest id holding it) and the winning lane pops its head.
+// lane j holding experts j + 2^LGS m (m < 4): h[m], hid[m] its logits and ids
+// (NaN and kNoExpert where it has none).  Every lane of the segment ends with
+// the chosen logits and ids in round order.  The lane sorts its four (logit,
+// id) pairs once, then each round reduces the heads of the segment's lanes
+// (the largest logit, then the lowest id holding it) and the winning lane pops
+// its head.
 template <int LGS, int K8 = 8>
-__device__ __forceinline__ void topk_rounds_sorted(const double* lt, int E, int k, int j, double (&val)[K8],
-                                                   int (&cid)[K8]) {
-  double h[4];
-  int hid[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int e2 = j + (m << LGS);
-    const double x = lt[min(e2, E - 1)];
-    h[m] = e2 < E ? x : __builtin_nan("");
-    hid[m] = e2 < E ? e2 : kNoExpert;
-  }
+__device__ __forceinline__ void topk_rounds_heads(double (&h)[4], int (&hid)[4], int k, double (&val)[K8],
+                                                  int (&cid)[K8]) {
   order_pair(h[0], hid[0], h[1], hid[1]);
   order_pair(h[2], hid[2], h[3], hid[3]);
   order_pair(h[0], hid[0], h[2], hid[2]);
@@ -112,6 +103,22 @@ __device__ __forceinline__ void topk_rounds_sorted(const double* lt, int E, int 
       hid[3] = pop ? kNoExpert : hid[3];
     }
   }
+}
+
+// The same with the token's E <= 4 * 2^LGS logits in LDS (lt).
+template <int LGS, int K8 = 8>
+__device__ __forceinline__ void topk_rounds_sorted(const double* lt, int E, int k, int j, double (&val)[K8],
+                                                   int (&cid)[K8]) {
+  double h[4];
+  int hid[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e2 = j + (m << LGS);
+    const double x = lt[min(e2, E - 1)];
+    h[m] = e2 < E ? x : __builtin_nan("");
+    hid[m] = e2 < E ? e2 : kNoExpert;
+  }
+  topk_rounds_heads<LGS>(h, hid, k, val, cid);
 }
 
 // The same for more than four experts per lane: each round scans the lane's
