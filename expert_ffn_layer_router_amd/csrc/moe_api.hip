@@ -105,6 +105,9 @@ bool api_check_handle(moe_handle h, const moe_config** cfg) {
 #ifndef MOE_DENSE_IDLE_MAX
 #define MOE_DENSE_IDLE_MAX 0.02  // dense tiles while an expert without routed rows is at most this likely
 #endif
+#ifndef MOE_ROUTER_SMALL_K
+#define MOE_ROUTER_SMALL_K 2048  // few-token router: k per block (each wave one 512-k pass)
+#endif
 #ifndef MOE_FUSED_COMBINE_MAX_T
 // Up to this T the down kernel's last blocks run the combine; above it a
 // kernel of its own (after a launch gap) beats them: the last block of a
@@ -135,8 +138,12 @@ void make_plan(const moe_config& c, int T, Plan* p) {
   p->fused_combine = p->fused_small && T <= MOE_FUSED_COMBINE_MAX_T;
   if (T <= kStreamMaxTokens) {
     p->router_split = 0;
-    // one 512-k pass per wave: k-split in multiples of 128, up to kRouterSmallMaxSplit
-    p->small_split = largest_divisor_at_most(c.d_model / 128, std::max(1, std::min(kRouterSmallMaxSplit, c.d_model / 2048)));
+    // one 512-k pass per wave (k-split in multiples of 128, up to
+    // kRouterSmallMaxSplit); with several token groups, two passes and half the
+    // blocks, whose finish then reloads half the partial logits (phi35_skew
+    // router 13.5 -> 12.5 us; with one token group, fine_decode, 12.7 -> 13.2)
+    const int kblock = MOE_ROUTER_SMALL_K * (T > kRouterTokTile ? 2 : 1);
+    p->small_split = largest_divisor_at_most(c.d_model / 128, std::max(1, std::min(kRouterSmallMaxSplit, c.d_model / kblock)));
   } else {
     // 64-token x router_tile_experts(E) tiles; split k (in multiples of 32) until about
     // MOE_ROUTER_BLOCKS blocks
