@@ -1,5 +1,7 @@
-// Weighted scatter-back of the expert outputs (many-token path; with few
-// tokens it is fused into the down GEMM).
+// Weighted scatter-back of the expert outputs: combine_kernel for the
+// many-token path (bf16 rows), combine_partials_kernel for the few-token path
+// above 8 tokens (the down GEMM's fp32 split partials); up to 8 tokens the
+// down GEMM's last blocks run the same sums themselves.
 //
 // Strata page, section 4.2: the regrouped rows go back to their tokens after
 // the group GEMM.  Written as a gather: out[t] = sum_j w[t,j] * y[inv[t*k+j]]
