@@ -279,28 +279,6 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
     const int grow = GATEUP ? a.perm[pbase + rr] / a.topk : pbase + rr;
     gsrc = a.gsum + (size_t)grow * a.gsum_stride;
   }
-  // row sums of A for the zero-point term
-  if (tid < kBM) {
-    float v = 0.0f;
-    if (tid < rows) {
-      if (GATEUP) {
-        v = a.xsum[a.perm[pbase + tid] / a.topk];
-      } else {
-        const float* hp = a.hsum_part + (size_t)(pbase + tid) * a.hparts;
-        int i = 0;
-        for (; i + 8 <= a.hparts; i += 8) {  // 8 loads in flight
-          float t[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) t[u] = hp[i + u];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) v += t[u];
-        }
-        for (; i < a.hparts; ++i) v += hp[i];
-      }
-    }
-    rowsum[tid] = v;
-  }
-
   auto issue = [&](int st) {
     char* buf = smem + (st % kNBuf) * kStage;
 #pragma unroll
@@ -345,6 +323,33 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
   for (int st = 0; st < kNBuf - 1; ++st)
     if (st < nst) issue(st);
+  // Row sums of A for the zero-point term, loaded while the first stages are
+  // in flight.  Gate/up: one token sum per row.  Down: the gate/up epilogue's
+  // partial sums of h per 128 columns, hparts per row; the kThreads / kBM
+  // threads of a row take contiguous runs of them with all loads of a batch
+  // of 32 issued together (one round trip for up to 32 per thread), then add
+  // the runs in a fixed order.
+  if constexpr (GATEUP) {
+    if (tid < kBM) rowsum[tid] = tid < rows ? a.xsum[a.perm[pbase + tid] / a.topk] : 0.0f;
+  } else {
+    constexpr int kPer = kThreads / kBM;  // threads per row: 2 or 4, adjacent lanes
+    static_assert(kPer * kBM == kThreads && (kPer == 1 || kPer == 2 || kPer == 4), "threads per row");
+    const int r = tid / kPer, part = tid % kPer;
+    const int run = (a.hparts + kPer - 1) / kPer;
+    const int i0 = min(a.hparts, part * run), i1 = min(a.hparts, i0 + run);
+    const float* hp = a.hsum_part + (size_t)(pbase + (r < rows ? r : 0)) * a.hparts;
+    float v = 0.0f;
+    for (int i = i0; i < i1; i += 32) {
+      float t[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) t[u] = i + u < i1 ? hp[i + u] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) v += t[u];
+    }
+    if (kPer >= 2) v += __shfl_xor(v, 1, 64);
+    if (kPer >= 4) v += __shfl_xor(v, 2, 64);
+    if (part == 0) rowsum[r] = r < rows ? v : 0.0f;
+  }
   // The main loop for ML live row blocks of 32 (a tile's last rows may be
   // missing; their products are skipped), instantiated for each ML so that
   // the loop carries no branches.

@@ -368,6 +368,31 @@ def test_one_hot_expert_takes_every_token(T):
     assert_out_close(res["out"], ref["out"])
 
 
+@pytest.mark.parametrize("T,E,k,slots,kind,zipf,group", [(300, 2, 2, 2, "identity", 0.0, 0),
+                                                            (400, 2, 2, 2, "perm", 0.0, 0),
+                                                            (513, 2, 2, 2, "identity", 0.0, 0),
+                                                            (500, 3, 2, 5, "sparse", 1.0, 0),
+                                                            (700, 4, 2, 4, "perm", 1.2, 0),
+                                                            (400, 2, 2, 2, "identity", 0.0, 128)])
+def test_prefill_ragged_row_tiles(T, E, k, slots, kind, zipf, group):
+    """Prefill layers (d = d_ff = 256) whose experts end in ragged 128-row
+    tiles: 44 rows after two full tiles (k = E: every token in every group),
+    16 rows, a lone row after four full tiles, and Zipf-skewed groups over a
+    permuted or sparse slot pool; one grouped-scale case."""
+    require_gpu()
+    shape = synth.LayerShape(T, 256, 256, E, k, slots, kind, zipf, 0, 4, group)
+    w = synth.make_weights(shape, seed=11)
+    x = synth.make_hidden(T, 256, seed=11)
+    case = synth.Case("ragged_prefill", shape, 11, x, w)
+    say(f"ragged prefill tiles: T={T} E={E} k={k} slots={slots}/{kind} zipf={zipf} group={group}")
+    res = GpuLayer(shape, w, max_tokens=T).run(x)
+    ref = _oracle(case)
+    check_routing(res, ref)
+    assert res["flags"] == 0
+    assert_out_close(res["out"], ref["out"])
+    say(f"ragged prefill tiles: ok, rows per expert {ref['counts'].tolist()}")
+
+
 def test_layers_graph_at_the_benchmarked_decode_shape_matches_the_oracle():
     """The graph bench.py times: several Mixtral-shaped decode layers (T = 16,
     d = 4096, d_ff = 14336, E = 8, top-2) back to back in one HIP graph, each
