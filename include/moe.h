@@ -187,7 +187,9 @@ moe_status moe_graph_capture(moe_handle h, int32_t T, const uint16_t *hidden, co
                              const float *router_bias, const int32_t *slot_table, const moe_weights *w,
                              uint16_t *out, void *workspace, size_t workspace_bytes, moe_stream stream);
 
-/* Replays the captured graph on `stream`.  MOE_ERR_BAD_STATE without a capture. */
+/* Replays the captured graph on `stream`.  MOE_ERR_BAD_STATE without a capture,
+ * or when the current device is not the one the graph was captured on (its
+ * kernels and pointers belong to that device). */
 moe_status moe_graph_launch(moe_handle h, moe_stream stream);
 
 /* Waits for `stream`, then reads the MOE_FLAG_* bits the last forward on
