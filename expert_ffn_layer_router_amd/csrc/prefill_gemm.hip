@@ -117,6 +117,21 @@ __device__ __forceinline__ int spos(int row, int c) {
   return c ^ ((row >> kShift) & (NC - 1));
 }
 
+// Sum over the lane's row of 16 lanes: partners by lane ^ 1, lane ^ 2, then
+// the half-row and row mirrors (DPP); every lane of the row ends with the same
+// sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_partner<0xB1>(v);
+  v += dpp_partner<0x4E>(v);
+  v += dpp_partner<0x141>(v);
+  v += dpp_partner<0x140>(v);
+  return v;
+}
+
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                  0, 0);
@@ -208,9 +223,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
   // compiler's alias information makes every LDS read wait for all
   // direct-to-LDS copies in flight (next stages included); the explicit
   // vmcnt waits below order the reads instead.
-  __shared__ __attribute__((aligned(1024))) char smem[kNBuf * kStage + (1 + WN) * kBM * 4];
-  float* rowsum = reinterpret_cast<float*>(smem + kNBuf * kStage);       // [kBM]
-  float (*hpart)[kBM] = reinterpret_cast<float (*)[kBM]>(rowsum + kBM);  // [WN][kBM]
+  __shared__ __attribute__((aligned(1024))) char smem[kNBuf * kStage + kBM * 4];
+  float* rowsum = reinterpret_cast<float*>(smem + kNBuf * kStage);  // [kBM]
   const int ntiles = *a.num_tiles;
   const int tile = blockIdx.y;
   if (tile >= ntiles) return;
@@ -583,7 +597,6 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
     constexpr int kCols = kWRows / 2;  // output columns of the block
     static_assert(kBM * kCols * 2 <= kNBuf * kStage, "h tile fits the stage ring");
     uint16_t* htile = reinterpret_cast<uint16_t*>(smem);  // [kBM][kCols], columns in h_phys_col order
-    float psum[MI][16];
 #pragma unroll
     for (int jj = 0; jj < HJ; ++jj) {
       const int nl = 32 * HJ * wn + 32 * jj + l32;  // column inside the block (n0 is a multiple of 8)
@@ -602,46 +615,33 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
           const float xs = rowsum[row];
           const float g = sg * (acc[i][jj][e] - cg * xs);
           const float u = su * (acc[i][jj + HJ][e] - cu * xs);
-          const uint16_t hb = f32_to_bf16(silu(g) * u);
-          psum[i][e] = (jj == 0 ? 0.0f : psum[i][e]) + bf16_to_f32(hb);
-          htile[row * kCols + hcol] = hb;
+          htile[row * kCols + hcol] = f32_to_bf16(silu(g) * u);
         }
       }
     }
-    // sum each row's partials over the 32 lanes holding its columns, then over the WN waves
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = psum[i][e];
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off, 32);
-        psum[i][e] = v;
-      }
-    if (l32 == 0) {
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) hpart[wn][32 * MI * wm + 32 * i + 8 * (e / 4) + 4 * hh + (e % 4)] = psum[i][e];
-    }
     lds_barrier();
+    // Copy-out in whole-row 16-byte chunks; thread c takes chunk c % kChunks of
+    // row c / kChunks, so the 16 chunks of a 128-column group (a group of the
+    // grouped formats) are the 16 lanes of one DPP row: each thread adds its
+    // chunk's 8 bf16 values of h and the row of lanes sums them, giving the
+    // down GEMM the per-row sums of h per 128 columns for its zero-point term.
+    // Every row of the tile takes part (uniform trip count for the
+    // exchanges); only the tile's rows are stored.
     constexpr int kChunks = kCols / 8;  // 16-byte chunks per row
-    for (int c = tid; c < rows * kChunks; c += kThreads) {
+    constexpr int kGroups = kCols / kQGroup;
+    static_assert(kGroups * kQGroup == kCols && kThreads % kChunks == 0 && kQGroup / 8 == 16,
+                  "a group of 128 columns is one row of 16 lanes");
+#pragma unroll 2
+    for (int c = tid; c < kBM * kChunks; c += kThreads) {
       const int r = c / kChunks, q = c % kChunks;
-      *reinterpret_cast<u32x4*>(a.h + (size_t)(pbase + r) * a.dff + n0 + 8 * q) =
-          *reinterpret_cast<const u32x4*>(htile + r * kCols + 8 * q);
-    }
-    // per 128 columns (a group of the grouped formats): the sum of its waves' parts
-    constexpr int kGroups = kCols / kQGroup, kWavesPerGroup = WN / kGroups;
-    static_assert(kGroups * kQGroup == kCols && kWavesPerGroup * 32 * HJ == kQGroup, "whole groups per wave set");
-    if (tid < rows && tid < kBM) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(htile + r * kCols + 8 * q);
+      if (r < rows) *reinterpret_cast<u32x4*>(a.h + (size_t)(pbase + r) * a.dff + n0 + 8 * q) = v;
+      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+      float cs = 0.0f;
 #pragma unroll
-      for (int g = 0; g < kGroups; ++g) {
-        float v = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWavesPerGroup; ++w) v += hpart[g * kWavesPerGroup + w][tid];
-        a.hsum_part[(size_t)(pbase + tid) * a.hparts + blockIdx.x * kGroups + g] = v;
-      }
+      for (int i = 0; i < 4; ++i) cs += __uint_as_float(vw[i] << 16) + __uint_as_float(vw[i] & 0xFFFF0000u);
+      cs = row16_sum(cs);
+      if (r < rows && q % 16 == 0) a.hsum_part[(size_t)(pbase + r) * a.hparts + blockIdx.x * kGroups + q / 16] = cs;
     }
   } else if constexpr (WM == 1) {
     // one pass per 32-row block: every wave holds all rows of the block
