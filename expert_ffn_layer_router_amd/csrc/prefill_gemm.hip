@@ -341,8 +341,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
   // in flight.  Gate/up: one token sum per row.  Down: the gate/up epilogue's
   // partial sums of h per 128 columns, hparts per row; the kThreads / kBM
   // threads of a row take contiguous runs of them with all loads of a batch
-  // of 32 issued together (one round trip for up to 32 per thread), then add
-  // the runs in a fixed order.
+  // of 32 issued together (one round trip for up to 32 per thread; 16-byte
+  // loads when the runs are whole 16-byte groups), then add the runs in a
+  // fixed order.
   if constexpr (GATEUP) {
     if (tid < kBM) rowsum[tid] = tid < rows ? a.xsum[a.perm[pbase + tid] / a.topk] : 0.0f;
   } else {
@@ -353,12 +354,24 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
     const int i0 = min(a.hparts, part * run), i1 = min(a.hparts, i0 + run);
     const float* hp = a.hsum_part + (size_t)(pbase + (r < rows ? r : 0)) * a.hparts;
     float v = 0.0f;
-    for (int i = i0; i < i1; i += 32) {
-      float t[32];
+    if (a.hparts % (4 * kPer) == 0) {
+      // rows of whole 16-byte groups and runs of them: 16-byte loads
+      for (int i = i0; i < i1; i += 32) {
+        float4 t[8];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) t[u] = i + u < i1 ? hp[i + u] : 0.0f;
+        for (int u = 0; u < 8; ++u)
+          t[u] = i + 4 * u < i1 ? *reinterpret_cast<const float4*>(hp + i + 4 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int u = 0; u < 32; ++u) v += t[u];
+        for (int u = 0; u < 8; ++u) v += ((t[u].x + t[u].y) + t[u].z) + t[u].w;
+      }
+    } else {
+      for (int i = i0; i < i1; i += 32) {
+        float t[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) t[u] = i + u < i1 ? hp[i + u] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 32; ++u) v += t[u];
+      }
     }
     if (kPer >= 2) v += __shfl_xor(v, 1, 64);
     if (kPer >= 4) v += __shfl_xor(v, 2, 64);
