@@ -377,6 +377,24 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
     if (kPer >= 4) v += __shfl_xor(v, 2, 64);
     if (part == 0) rowsum[r] = r < rows ? v : 0.0f;
   }
+  // Per-row formats: the scales and zero-points of this wave's output
+  // columns (gate/up: gate and up of HJ column blocks; down: NJW blocks),
+  // loaded before the main loop so that the epilogue does not wait for them.
+  constexpr int kEpi = GATEUP ? HJ : NJW;
+  uint16_t es0[kEpi], ez0[kEpi], es1[kEpi], ez1[kEpi];
+#pragma unroll
+  for (int t = 0; t < kEpi; ++t) {
+    es0[t] = ez0[t] = es1[t] = ez1[t] = 0;
+    if constexpr (!GROUPED) {
+      const size_t sidx = (size_t)slot * ncols + n0 + (GATEUP ? 32 * HJ * wn : 32 * NJW * wn) + 32 * t + l32;
+      es0[t] = a.s0[sidx];
+      ez0[t] = a.z0[sidx];
+      if constexpr (GATEUP) {
+        es1[t] = a.s1[sidx];
+        ez1[t] = a.z1[sidx];
+      }
+    }
+  }
   // The main loop for ML live row blocks of 32 (a tile's last rows may be
   // missing; their products are skipped), instantiated for each ML so that
   // the loop carries no branches.
@@ -613,12 +631,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
     for (int jj = 0; jj < HJ; ++jj) {
       const int nl = 32 * HJ * wn + 32 * jj + l32;  // column inside the block (n0 is a multiple of 8)
-      const size_t sidx = (size_t)slot * ncols + n0 + nl;
       // grouped formats: the weights were dequantised in full already
-      const float sg = GROUPED ? cur_s[jj] : fp16_to_f32(a.s0[sidx]);
-      const float cg = GROUPED ? 0.0f : kBias + fp16_to_f32(a.z0[sidx]);
-      const float su = GROUPED ? cur_s[jj + HJ] : fp16_to_f32(a.s1[sidx]);
-      const float cu = GROUPED ? 0.0f : kBias + fp16_to_f32(a.z1[sidx]);
+      const float sg = GROUPED ? cur_s[jj] : fp16_to_f32(es0[jj]);
+      const float cg = GROUPED ? 0.0f : kBias + fp16_to_f32(ez0[jj]);
+      const float su = GROUPED ? cur_s[jj + HJ] : fp16_to_f32(es1[jj]);
+      const float cu = GROUPED ? 0.0f : kBias + fp16_to_f32(ez1[jj]);
       const int hcol = h_phys_col(nl);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
@@ -663,9 +680,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
     float sd[NJW], cd[NJW];
 #pragma unroll
     for (int j = 0; j < NJW; ++j) {
-      const size_t sidx = (size_t)slot * ncols + n0 + 32 * NJW * wn + 32 * j + l32;
-      sd[j] = GROUPED ? cur_s[j] : fp16_to_f32(a.s0[sidx]);
-      cd[j] = GROUPED ? 0.0f : kBias + fp16_to_f32(a.z0[sidx]);
+      sd[j] = GROUPED ? cur_s[j] : fp16_to_f32(es0[j]);
+      cd[j] = GROUPED ? 0.0f : kBias + fp16_to_f32(ez0[j]);
     }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -699,9 +715,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
     for (int j = 0; j < NJW; ++j) {
       const int n = n0 + 32 * NJW * wn + 32 * j + l32;
-      const size_t sidx = (size_t)slot * ncols + n;
-      const float sd = GROUPED ? cur_s[j] : fp16_to_f32(a.s0[sidx]);
-      const float cd = GROUPED ? 0.0f : kBias + fp16_to_f32(a.z0[sidx]);
+      const float sd = GROUPED ? cur_s[j] : fp16_to_f32(es0[j]);
+      const float cd = GROUPED ? 0.0f : kBias + fp16_to_f32(ez0[j]);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
