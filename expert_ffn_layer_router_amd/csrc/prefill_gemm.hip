@@ -53,6 +53,10 @@ constexpr int kQGroup = 128;            // k per (s, z) group of the grouped for
 #ifndef MOE_PF_GU_HANDOVER
 #define MOE_PF_GU_HANDOVER 1
 #endif
+// ... with each k-step's B fragments widened one step ahead
+#ifndef MOE_PF_GU_WIDEN_AHEAD
+#define MOE_PF_GU_WIDEN_AHEAD 1
+#endif
 #ifndef MOE_PF_DN_BK4
 #define MOE_PF_DN_BK4 64   // k per stage of the int4 down blocks
 #endif
@@ -555,12 +559,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
       }
     };
     static_assert(kNS % 2 == 0, "the last step's A fragments are in av1, the next stage's first in av0");
-    u32x4 bq[NJW][kCPR / 2], av0[MI], av1[MI];
+    u32x4 bq[NJW][kCPR / 2], av0[MI], av1[MI], bc[NJW];
     wait_vmem<0>();
     lds_barrier();
     if (1 < nst) issue(1);
     read_b(smem, bq);
     read_a(smem, 0, av0);
+#if MOE_PF_GU_WIDEN_AHEAD
+#pragma unroll
+    for (int j = 0; j < NJW; ++j) bc[j] = widen(bq, j, 0);
+#endif
     for (int st = 0; st < nst; ++st) {
       const char* buf = smem + (st % 2) * kStage;
 #pragma unroll
@@ -568,6 +576,22 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
         u32x4(&cur)[MI] = (s & 1) ? av1 : av0;
         u32x4(&nxt)[MI] = (s & 1) ? av0 : av1;
         read_a(buf, s + 1, nxt);
+#if MOE_PF_GU_WIDEN_AHEAD
+        // the next step's B fragments are widened, and its A fragments read,
+        // before this step's products: no product waits for a widening
+        // instruction or a read issued just before it
+        u32x4 bn[NJW];
+#pragma unroll
+        for (int j = 0; j < NJW; ++j) bn[j] = widen(bq, j, s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NJW; ++j)
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            if (i < ML) acc[i][j] = mfma32(cur[i], bc[j], acc[i][j]);
+#pragma unroll
+        for (int j = 0; j < NJW; ++j) bc[j] = bn[j];
+#else
 #pragma unroll
         for (int j = 0; j < NJW; ++j) {
           const u32x4 b = widen(bq, j, s);
@@ -575,10 +599,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
           for (int i = 0; i < MI; ++i)
             if (i < ML) acc[i][j] = mfma32(cur[i], b, acc[i][j]);
         }
+#endif
       }
       u32x4 bl[NJW];
 #pragma unroll
-      for (int j = 0; j < NJW; ++j) bl[j] = widen(bq, j, kNS - 1);
+      for (int j = 0; j < NJW; ++j) bl[j] = MOE_PF_GU_WIDEN_AHEAD ? bc[j] : widen(bq, j, kNS - 1);
       // Unconditional, so that no control-flow merge makes the compiler wait
       // for these reads before the products below: after the last stage the
       // reads take the other buffer's stale contents (unused) and the barrier
@@ -595,6 +620,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
         for (int i = 0; i < MI; ++i)
           if (i < ML) acc[i][j] = mfma32(av1[i], bl[j], acc[i][j]);
+#if MOE_PF_GU_WIDEN_AHEAD
+#pragma unroll
+      for (int j = 0; j < NJW; ++j) bc[j] = widen(bq, j, 0);
+#endif
       // the copies of the stage after next, into the buffer just retired
       // (issued after the products, so that the reads and products above
       // stay in one block)
