@@ -61,7 +61,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 // Few tokens, the down kernel's fp32 partials ypart[split][p][d]: per output
 // the rows j = 0..k-1 in order, each the sum of its splits in split order,
 // weighted -- the same operations, in the same order, as the combine the down
-// kernel runs in its last blocks.  One thread: 4 columns of one token.
+// kernel runs in its last blocks.  One thread: 4 columns of one token.  All k
+// row indices and weights are loaded first, then each split's k loads are
+// issued together (k <= 8 is uniform: no divergence), so the dependent round
+// trips are 1 + nsplit instead of k (1 + nsplit).
 __global__ __launch_bounds__(256) void combine_partials_kernel(const float* __restrict__ ypart, int R, int d,
                                                                int nsplit, const int32_t* __restrict__ inv,
                                                                const float* __restrict__ topk_w, int T, int k,
@@ -70,22 +73,43 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float* __re
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * per_row) return;
   const int t = idx / per_row, c = (idx % per_row) * 4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int p = inv[t * k + j];
-    const float w = topk_w[t * k + j];
-    float4 v = *reinterpret_cast<const float4*>(ypart + (size_t)p * d + c);
-    for (int sp = 1; sp < nsplit; ++sp) {
-      const float4 u = *reinterpret_cast<const float4*>(ypart + ((size_t)sp * R + p) * d + c);
-      v.x += u.x;
-      v.y += u.y;
-      v.z += u.z;
-      v.w += u.w;
+  int pos[8];
+  float wt[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < k) {
+      pos[j] = inv[t * k + j];
+      wt[j] = topk_w[t * k + j];
     }
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
+  }
+  float4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < k) v[j] = *reinterpret_cast<const float4*>(ypart + (size_t)pos[j] * d + c);
+  for (int sp = 1; sp < nsplit; ++sp) {
+    float4 u[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) u[j] = *reinterpret_cast<const float4*>(ypart + ((size_t)sp * R + pos[j]) * d + c);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        v[j].x += u[j].x;
+        v[j].y += u[j].y;
+        v[j].z += u[j].z;
+        v[j].w += u[j].w;
+      }
+    }
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < k) {
+      acc.x = fmaf(wt[j], v[j].x, acc.x);
+      acc.y = fmaf(wt[j], v[j].y, acc.y);
+      acc.z = fmaf(wt[j], v[j].z, acc.z);
+      acc.w = fmaf(wt[j], v[j].w, acc.w);
+    }
   }
   uint2 o;
   o.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
