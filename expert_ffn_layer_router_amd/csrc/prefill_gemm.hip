@@ -690,7 +690,6 @@ __global__ __launch_bounds__(64 * NW, OCC) void prefill_gemm_kernel(PrefillArgs 
     constexpr int kGroups = kCols / kQGroup;
     static_assert(kGroups * kQGroup == kCols && kThreads % kChunks == 0 && kQGroup / 8 == 16,
                   "a group of 128 columns is one row of 16 lanes");
-#pragma unroll 2
     for (int c = tid; c < kBM * kChunks; c += kThreads) {
       const int r = c / kChunks, q = c % kChunks;
       const u32x4 v = *reinterpret_cast<const u32x4*>(htile + r * kCols + 8 * q);
